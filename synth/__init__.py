@@ -1,0 +1,346 @@
+"""Seeded synthetic inputs for the QSVD joint-QKV latent-attention hot path.
+
+This module is shared by the tests, the benchmark and the CPU oracle's callers.
+It draws random numbers and assembles the synthetic *inputs* of the hot path
+(a compressed attention layer and its cached latents).  It performs none of the
+hot path's own steps: no Walsh-Hadamard butterflies, no activation or latent
+quantisation, no projection kernels, no attention.  Those live, independently,
+in the HIP library and in the float64 oracle.
+
+What it builds, following the method as described on the QSVD pages
+(NeurIPS 2025 paper notes, "Key design"; QSVD digest, "Method, Step 1"):
+
+* the original weights W_concat = [W_Q | W_K | W_V] = U diag(sigma) V^T, with
+  Haar-random orthonormal U, V (QR of a seeded Gaussian, signs fixed so that
+  diag(R) > 0) and sigma_i = i^-p, so the joint SVD is known exactly;
+* the beta-split factors W^d = U_r Sigma_r^beta (E x r) and
+  W^u = Sigma_r^(1-beta) V_r^T (r x 3E), split by columns into W^u_q, W^u_k,
+  W^u_v (Q, K, V order);
+* offline folding of the orthogonal rotations into the stored weights, as in
+  Y = (X H1^T)(H1 W^d H2^T)(H2 W^u) (QSVD notes, "Key design", quantisation
+  scheme): H is block-diagonal normalised Sylvester-Hadamard with 128-wide
+  blocks, built here with ``scipy.linalg.hadamard``;
+* offline per-output-column int8 weight codes (weights are quantised once,
+  before inference);
+* activations X ~ N(0, 1) with a seeded set of outlier channels scaled up
+  (channel-wise outliers, QSVD notes "Motivation");
+* bf16 latent caches drawn as C = X W^d' (the configs describe the cache as
+  latents of such activations), rounded float64 -> float32 -> bf16 (RNE).
+
+Every array is float64 until it is cast; bf16 is returned as raw uint16 bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import scipy.linalg
+
+__all__ = [
+    "Config", "CONFIGS", "rng", "haar_columns", "spectrum", "outlier_channels",
+    "activations", "Layer", "make_layer", "block_hadamard", "to_bf16_bits",
+    "bf16_bits_to_f64", "int8_columns", "decode_case", "DecodeCase",
+    "c4_ranks", "c4_layer", "sharpen_query",
+]
+
+
+# ----------------------------------------------------------------------------
+# Workload table (shapes of LLaVA-v1.5 7B / 13B attention layers, tiny case)
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Config:
+    idx: int
+    name: str
+    E: int
+    heads: int
+    d: int
+    r: int
+    b: int
+    L: int
+    p: float              # sigma_i = i^-p
+    beta: float | None    # None: one draw from U[0.3, 0.7]
+    outlier_frac: float
+    outlier_gain: float
+    hadamard: int         # 0: H1 = H2 = I; 128: block Walsh-Hadamard
+    cache: str            # "f32", "bf16", "i4" (int4, group 128), "prefill"
+
+
+CONFIGS = {
+    0: Config(0, "tiny-fp32 E256 r96 b1 L512", 256, 4, 64, 96, 1, 512, 0.6, 0.5,
+              0.01, 20.0, 0, "f32"),
+    1: Config(1, "llava-v1.5-7b bf16 E4096 r1536 b16 L8192", 4096, 32, 128, 1536, 16,
+              8192, 0.5, 0.5, 0.01, 50.0, 128, "bf16"),
+    2: Config(2, "llava-v1.5-7b W8A4 E4096 r768 b16 L8192", 4096, 32, 128, 768, 16,
+              8192, 0.5, None, 0.01, 50.0, 128, "i4"),
+    3: Config(3, "llava-v1.5-13b bf16 E5120 r2304 b8 L16384", 5120, 40, 128, 2304, 8,
+              16384, 0.4, 0.5, 0.005, 100.0, 128, "bf16"),
+    4: Config(4, "prefill W8A8 M16384 E4096 24 layers", 4096, 32, 128, 1536, 4,
+              4096, 0.5, 0.5, 0.01, 50.0, 128, "prefill"),
+}
+
+
+# ----------------------------------------------------------------------------
+# Random streams
+# ----------------------------------------------------------------------------
+def rng(*key: int) -> np.random.Generator:
+    """PCG64 stream keyed by a tuple of non-negative ints (seed-sequence entropy)."""
+    return np.random.default_rng(np.random.SeedSequence([int(k) for k in key]))
+
+
+# stream ids
+_U, _V, _OUTLIER, _BETA, _X, _XNEW, _PERM = 1, 2, 3, 4, 10, 11, 12
+
+
+def haar_columns(n: int, k: int, g: np.random.Generator) -> np.ndarray:
+    """First k columns of a Haar-random n x n orthogonal matrix (float64).
+
+    The Gaussian is drawn column by column (k rows of length n, transposed), so
+    the first k columns are the same whatever k is; QR with diag(R) > 0.
+    """
+    G = g.standard_normal((k, n)).T
+    Q, R = np.linalg.qr(G)
+    s = np.sign(np.diag(R))
+    s[s == 0] = 1.0
+    return Q * s
+
+
+def spectrum(p: float, n: int) -> np.ndarray:
+    """sigma_i = i^-p for i = 1..n (descending)."""
+    return np.arange(1, n + 1, dtype=np.float64) ** (-p)
+
+
+def outlier_channels(E: int, frac: float, g: np.random.Generator) -> np.ndarray:
+    """round(frac * E) channel indices from a seeded permutation (sorted)."""
+    n = int(round(frac * E))
+    return np.sort(g.permutation(E)[:n])
+
+
+def activations(rows: int, E: int, channels: np.ndarray, gain: float,
+                g: np.random.Generator) -> np.ndarray:
+    """X ~ N(0, 1) of shape [rows][E] with the given channels multiplied by gain."""
+    X = g.standard_normal((rows, E))
+    X[:, channels] *= gain
+    return X
+
+
+def block_hadamard(n: int, block: int) -> np.ndarray:
+    """Block-diagonal normalised Sylvester-Hadamard (n x n, float64); I if block == 0."""
+    if block == 0:
+        return np.eye(n)
+    assert n % block == 0
+    Hb = scipy.linalg.hadamard(block).astype(np.float64) / math.sqrt(block)
+    return np.kron(np.eye(n // block), Hb)
+
+
+def _apply_block_hadamard_left(H_block: int, M: np.ndarray) -> np.ndarray:
+    """(blockdiag(H) @ M) without forming the n x n matrix."""
+    if H_block == 0:
+        return M.copy()
+    n = M.shape[0]
+    Hb = scipy.linalg.hadamard(H_block).astype(np.float64) / math.sqrt(H_block)
+    out = np.empty_like(M)
+    for i in range(0, n, H_block):
+        out[i:i + H_block] = Hb @ M[i:i + H_block]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# bf16 / int8 storage helpers (input casting only)
+# ----------------------------------------------------------------------------
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32 (RNE) -> bf16 (RNE), returned as uint16 bits."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32)
+    u = u + (((u >> 16) & 1) + np.uint32(0x7FFF))
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f64(u: np.ndarray) -> np.ndarray:
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def int8_columns(W: np.ndarray):
+    """Offline symmetric per-column int8 weight codes: (codes int8 [rows][cols], scale f32 [cols]).
+
+    scale = max_k |W[k, n]| / 127 (float32), code = rint(W / scale) clipped to +-127.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    amax = np.abs(W).max(axis=0)
+    scale = (amax / 127.0).astype(np.float32)
+    s64 = scale.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s64 > 0, np.rint(W / np.where(s64 > 0, s64, 1.0)), 0.0)
+    return np.clip(q, -127, 127).astype(np.int8), scale
+
+
+# ----------------------------------------------------------------------------
+# The compressed layer
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class Layer:
+    E: int
+    r: int
+    beta: float
+    sigma: np.ndarray      # [E] full spectrum (rank(W_concat) <= E)
+    U: np.ndarray          # [E][k] first k >= r left singular vectors
+    V: np.ndarray          # [3E][k] first k >= r right singular vectors
+    Wd: np.ndarray         # [E][r]   = U_r Sigma_r^beta
+    Wu: np.ndarray         # [r][3E]  = Sigma_r^(1-beta) V_r^T
+
+    @property
+    def Wu_q(self):
+        return self.Wu[:, : self.E]
+
+    @property
+    def Wu_k(self):
+        return self.Wu[:, self.E: 2 * self.E]
+
+    @property
+    def Wu_v(self):
+        return self.Wu[:, 2 * self.E:]
+
+    def W_concat(self) -> np.ndarray:
+        """U diag(sigma) V^T over the columns generated (exact W_concat when k = E)."""
+        k = self.U.shape[1]
+        return (self.U * self.sigma[:k]) @ self.V.T
+
+
+def make_layer(E: int, r: int, p: float, beta: float, seed: tuple, k: int | None = None) -> Layer:
+    """Synthetic joint-QKV layer with known SVD; k = generated singular vectors (>= r)."""
+    k = r if k is None else k
+    assert r <= k <= E
+    U = haar_columns(E, k, rng(*seed, _U))
+    V = haar_columns(3 * E, k, rng(*seed, _V))
+    sigma = spectrum(p, E)
+    sr = sigma[:r]
+    Wd = U[:, :r] * sr ** beta
+    Wu = (sr ** (1.0 - beta))[:, None] * V[:, :r].T
+    return Layer(E, r, beta, sigma, U, V, Wd, Wu)
+
+
+def config_beta(cfg: Config) -> float:
+    if cfg.beta is not None:
+        return cfg.beta
+    return float(rng(1000 + cfg.idx, _BETA).uniform(0.3, 0.7))
+
+
+# ----------------------------------------------------------------------------
+# Decode cases
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class DecodeCase:
+    """Inputs of one decode step (all float64 or raw storage, CPU side).
+
+    cache   'f32'  : C [b][L][r] float32
+            'bf16' : C [b][L][r] uint16 bf16 bits
+            'i4'   : C_codes [b][L][r/2] uint8 packed nibbles, C_scales [b][L][r/128] float32
+                     (only when built through the quantised chain; see tests)
+    q       [b][heads][d] (float32 or bf16 bits)
+    Wu_k/Wu_v [r][E] stored weights (float32, bf16 bits or int8 codes) + optional column scales
+    """
+    E: int
+    heads: int
+    d: int
+    r: int
+    b: int
+    L: int
+    dtype: str
+    q: np.ndarray
+    C: np.ndarray
+    Wu_k: np.ndarray
+    Wu_v: np.ndarray
+    softmax_scale: float
+    X: list | None = None          # per-sequence activations [L+1][E] (float64), if kept
+    layer: Layer | None = None
+    channels: np.ndarray | None = None
+
+
+def decode_case(E: int, heads: int, d: int, r: int, b: int, L: int, *, dtype: str = "f32",
+                p: float = 0.6, beta: float = 0.5, outlier_frac: float = 0.01,
+                outlier_gain: float = 20.0, hadamard: int = 0, seed: int = 7,
+                keep_x: bool = False, k: int | None = None, seqs=None) -> DecodeCase:
+    """A decode step of the latent-attention layer at arbitrary shape.
+
+    The cache of sequence s holds the latents of X_s rows 0..L-1; the query of
+    sequence s is q = (x_new W^d) W^u_q with x_new = row L of X_s (one decode
+    query per sequence).  With hadamard = 128, H2 is folded into the stored
+    factors: C' = C H2^T (i.e. W^d' = W^d H2^T) and W^u' = H2 W^u.
+    ``seqs`` restricts generation to a subset of sequences (same values as in
+    the full batch).
+    """
+    assert E == heads * d
+    layer = make_layer(E, r, p, beta, (seed, 0), k=k)
+    channels = outlier_channels(E, outlier_frac, rng(seed, _OUTLIER))
+    Wd_rot = _apply_block_hadamard_left(hadamard, layer.Wd.T).T        # W^d H2^T
+    Wu_rot = _apply_block_hadamard_left(hadamard, layer.Wu)            # H2 W^u
+    seqs = range(b) if seqs is None else seqs
+    Cs, qs, Xs = [], [], []
+    for s in seqs:
+        X = activations(L + 1, E, channels, outlier_gain, rng(seed, _X, s))
+        C = X[:L] @ Wd_rot
+        q = (X[L] @ layer.Wd) @ layer.Wu_q                             # rotation-free
+        Cs.append(C)
+        qs.append(q.reshape(heads, d))
+        if keep_x:
+            Xs.append(X)
+    C = np.stack(Cs)
+    q = np.stack(qs)
+    Wu_k = Wu_rot[:, E:2 * E]
+    Wu_v = Wu_rot[:, 2 * E:]
+    if dtype == "f32":
+        cast = lambda a: np.asarray(a, np.float64).astype(np.float32)
+    elif dtype == "bf16":
+        cast = to_bf16_bits
+    else:
+        raise ValueError(dtype)
+    return DecodeCase(E, heads, d, r, len(qs), L, dtype, cast(q), cast(C), cast(Wu_k), cast(Wu_v),
+                      1.0 / math.sqrt(d), Xs if keep_x else None, layer, channels)
+
+
+def config_decode_case(cfg: Config, seqs=None, keep_x: bool = False, L: int | None = None) -> DecodeCase:
+    """The decode step of configs 0, 1 and 3 (float32 / bf16 caches)."""
+    assert cfg.cache in ("f32", "bf16")
+    return decode_case(cfg.E, cfg.heads, cfg.d, cfg.r, cfg.b, cfg.L if L is None else L,
+                       dtype=cfg.cache, p=cfg.p, beta=config_beta(cfg),
+                       outlier_frac=cfg.outlier_frac, outlier_gain=cfg.outlier_gain,
+                       hadamard=cfg.hadamard, seed=1000 + cfg.idx, keep_x=keep_x, seqs=seqs)
+
+
+def sharpen_query(q: np.ndarray, factor: float) -> np.ndarray:
+    """Test-only variant: scale the query so that the softmax is far from uniform."""
+    return np.asarray(q, np.float64) * factor
+
+
+# ----------------------------------------------------------------------------
+# Quantised-cache / prefill inputs (configs 2 and 4)
+# ----------------------------------------------------------------------------
+def quantised_layer_inputs(E: int, r: int, p: float, beta: float, hadamard: int, seed: tuple):
+    """Stored weights of the W8Ax path.
+
+    W^d' = H1 W^d quantised per output column to int8 (H2 is applied online to
+    the latent), W^u' = H2 W^u quantised per output column to int8.
+    Returns dict with Wd_q [E][r] int8, Wd_s [r] f32, Wu_{q,k,v} float64 rotated,
+    Wu_k_q/Wu_v_q [r][E] int8, Wu_k_s/Wu_v_s [E] f32, layer.
+    """
+    layer = make_layer(E, r, p, beta, seed)
+    Wd_h1 = _apply_block_hadamard_left(hadamard, layer.Wd)            # H1 W^d
+    Wd_q, Wd_s = int8_columns(Wd_h1)
+    Wu_rot = _apply_block_hadamard_left(hadamard, layer.Wu)           # H2 W^u
+    Wk_q, Wk_s = int8_columns(Wu_rot[:, E:2 * E])
+    Wv_q, Wv_s = int8_columns(Wu_rot[:, 2 * E:])
+    return dict(layer=layer, Wd_q=Wd_q, Wd_s=Wd_s, Wu_rot=Wu_rot,
+                Wu_k_q=Wk_q, Wu_k_s=Wk_s, Wu_v_q=Wv_q, Wu_v_s=Wv_s)
+
+
+def c4_ranks(seed: int = 1004) -> np.ndarray:
+    """Per-layer ranks for the 24-layer prefill chain: a fixed multiset
+    (2 x 512, 4 x 1024, 10 x 1536, 8 x 2048; sum 24 x 1536) in seeded order."""
+    ranks = np.array([512] * 2 + [1024] * 4 + [1536] * 10 + [2048] * 8)
+    return ranks[rng(seed, _PERM).permutation(len(ranks))]
+
+
+def c4_layer(l: int, r: int, E: int = 4096, p: float = 0.5, beta: float = 0.5, hadamard: int = 128):
+    """Stored int8 weights of prefill layer l (W^d' per column, [W^u_k | W^u_v] per column)."""
+    return quantised_layer_inputs(E, r, p, beta, hadamard, (100400 + l,))
+
