@@ -1,0 +1,343 @@
+// Host side of the C ABI: argument validation (before any HIP call), dispatch
+// to the kernel launchers, error mapping and the optional timing session.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "qsvd_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qsvd_status_t fail(qsvd_status_t s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+qsvd_status_t ok() {
+  g_last_error.clear();
+  return QSVD_OK;
+}
+
+qsvd_status_t device_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(QSVD_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+const char *dtype_name(int dt) {
+  switch (dt) {
+    case QSVD_F32: return "F32";
+    case QSVD_BF16: return "BF16";
+    case QSVD_I8: return "I8";
+    case QSVD_I4: return "I4";
+    default: return "?";
+  }
+}
+
+// ---------------------------------------------------------------- timing session
+struct TimingRecord {
+  const char *name;
+  hipEvent_t start, stop;
+};
+
+struct TimingSession {
+  bool active = false;
+  int max_launches = 0;
+  std::vector<hipEvent_t> pool;
+  std::vector<TimingRecord> records;
+};
+
+thread_local TimingSession g_timing;
+
+}  // namespace
+
+namespace qsvd {
+
+LaunchTimer::LaunchTimer(const char *name, hipStream_t stream) : slot_(-1), stream_(stream) {
+  TimingSession &t = g_timing;
+  if (!t.active || static_cast<int>(t.records.size()) >= t.max_launches) return;
+  const size_t i = t.records.size();
+  TimingRecord rec{name, t.pool[2 * i], t.pool[2 * i + 1]};
+  if (hipEventRecord(rec.start, stream) != hipSuccess) return;
+  t.records.push_back(rec);
+  slot_ = static_cast<int>(i);
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (slot_ < 0) return;
+  (void)hipEventRecord(g_timing.records[slot_].stop, stream_);
+}
+
+}  // namespace qsvd
+
+extern "C" {
+
+const char *qsvd_status_string(qsvd_status_t s) {
+  switch (s) {
+    case QSVD_OK: return "QSVD_OK";
+    case QSVD_ERR_INVALID: return "QSVD_ERR_INVALID: invalid argument";
+    case QSVD_ERR_UNSUPPORTED: return "QSVD_ERR_UNSUPPORTED: unsupported combination";
+    case QSVD_ERR_WORKSPACE: return "QSVD_ERR_WORKSPACE: workspace too small";
+    case QSVD_ERR_DEVICE: return "QSVD_ERR_DEVICE: HIP runtime error";
+    default: return "QSVD: unknown status";
+  }
+}
+
+const char *qsvd_last_error(void) { return g_last_error.c_str(); }
+
+qsvd_status_t qsvd_quantize_latent(const void *in, qsvd_dtype_t in_dtype, int64_t M, int32_t n,
+                                   int32_t hadamard_block, qsvd_dtype_t code_dtype, int32_t group,
+                                   void *codes, float *scales, void *hip_stream) {
+  if (in_dtype != QSVD_F32 && in_dtype != QSVD_BF16)
+    return fail(QSVD_ERR_INVALID, "quantize_latent: in_dtype %s (F32 or BF16)", dtype_name(in_dtype));
+  if (code_dtype != QSVD_I8 && code_dtype != QSVD_I4)
+    return fail(QSVD_ERR_INVALID, "quantize_latent: code_dtype %s (I8 or I4)", dtype_name(code_dtype));
+  if (hadamard_block != 0 && hadamard_block != 128)
+    return fail(QSVD_ERR_UNSUPPORTED, "quantize_latent: hadamard_block %d (0 or 128)", hadamard_block);
+  if (group != 0 && group != 128)
+    return fail(QSVD_ERR_UNSUPPORTED, "quantize_latent: group %d (0 or 128)", group);
+  if (M < 0) return fail(QSVD_ERR_INVALID, "quantize_latent: M = %lld < 0", (long long)M);
+  if (n <= 0 || n % 8 != 0 || n > 8192)
+    return fail(QSVD_ERR_INVALID, "quantize_latent: n = %d (positive, multiple of 8, <= 8192)", n);
+  if ((hadamard_block || group) && n % 128 != 0)
+    return fail(QSVD_ERR_INVALID, "quantize_latent: n = %d must be a multiple of 128", n);
+  if (M > (int64_t)0x7FFFFFFF * 4)
+    return fail(QSVD_ERR_INVALID, "quantize_latent: M = %lld too large", (long long)M);
+  if (M == 0) return ok();
+  if (!in || !codes || !scales) return fail(QSVD_ERR_INVALID, "quantize_latent: NULL pointer");
+  if (!aligned16(in) || !aligned16(codes) || !aligned4(scales))
+    return fail(QSVD_ERR_INVALID, "quantize_latent: misaligned pointer");
+  const hipError_t e = qsvd::launch_rotate_quant(
+      in, in_dtype == QSVD_BF16, M, n, hadamard_block == 128, code_dtype == QSVD_I4, group == 128,
+      codes, scales, static_cast<hipStream_t>(hip_stream));
+  return device_status(e, "quantize_latent");
+}
+
+qsvd_status_t qsvd_project(const void *X, qsvd_dtype_t x_dtype, const float *x_scale, int64_t M,
+                           int32_t E, const void *W_packed, qsvd_dtype_t w_dtype,
+                           const float *col_scale, int32_t r, void *C, qsvd_dtype_t c_dtype,
+                           void *hip_stream) {
+  if (x_dtype != QSVD_I8 && x_dtype != QSVD_BF16)
+    return fail(QSVD_ERR_UNSUPPORTED, "project: x_dtype %s (I8 or BF16)", dtype_name(x_dtype));
+  if (w_dtype != x_dtype)
+    return fail(QSVD_ERR_UNSUPPORTED, "project: w_dtype %s must equal x_dtype %s",
+                dtype_name(w_dtype), dtype_name(x_dtype));
+  if (c_dtype != QSVD_F32 && c_dtype != QSVD_BF16)
+    return fail(QSVD_ERR_INVALID, "project: c_dtype %s (F32 or BF16)", dtype_name(c_dtype));
+  if (M < 0) return fail(QSVD_ERR_INVALID, "project: M = %lld < 0", (long long)M);
+  if (E <= 0 || E % 64 != 0)
+    return fail(QSVD_ERR_INVALID, "project: E = %d (positive multiple of 64)", E);
+  if (r <= 0 || r % 16 != 0)
+    return fail(QSVD_ERR_INVALID, "project: r = %d (positive multiple of 16)", r);
+  if (x_dtype == QSVD_I8 && !x_scale)
+    return fail(QSVD_ERR_INVALID, "project: int8 X needs x_scale");
+  if (x_dtype == QSVD_BF16 && x_scale)
+    return fail(QSVD_ERR_INVALID, "project: bf16 X takes no x_scale");
+  if (M == 0) return ok();
+  if (!X || !W_packed || !C) return fail(QSVD_ERR_INVALID, "project: NULL pointer");
+  if (!aligned16(X) || !aligned16(W_packed) || !aligned16(C) ||
+      (x_scale && !aligned4(x_scale)) || (col_scale && !aligned4(col_scale)))
+    return fail(QSVD_ERR_INVALID, "project: misaligned pointer");
+  const int64_t tiles = ((M + 127) / 128) * ((r + 127) / 128);
+  if (tiles > 0x7FFFFFFF) return fail(QSVD_ERR_INVALID, "project: problem too large");
+  const hipError_t e = qsvd::launch_gemm(X, x_scale, x_dtype == QSVD_I8, M, E, W_packed, col_scale,
+                                         r, C, c_dtype == QSVD_BF16,
+                                         static_cast<hipStream_t>(hip_stream));
+  return device_status(e, "project");
+}
+
+qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int32_t cols,
+                               void *packed, void *hip_stream) {
+  int esz;
+  switch (dt) {
+    case QSVD_F32: esz = 4; break;
+    case QSVD_BF16: esz = 2; break;
+    case QSVD_I8: esz = 1; break;
+    default: return fail(QSVD_ERR_INVALID, "pack_weight: dtype %s", dtype_name(dt));
+  }
+  if (rows < 0 || cols < 0) return fail(QSVD_ERR_INVALID, "pack_weight: negative shape");
+  if (rows == 0 || cols == 0) return ok();
+  if (!W || !packed) return fail(QSVD_ERR_INVALID, "pack_weight: NULL pointer");
+  return device_status(qsvd::launch_transpose(W, esz, rows, cols, packed,
+                                              static_cast<hipStream_t>(hip_stream)),
+                       "pack_weight");
+}
+
+static qsvd_status_t validate_decode_shape(int32_t b, int64_t L, int32_t r, int32_t heads,
+                                           int32_t d, qsvd_dtype_t c_dtype, int32_t splits) {
+  if (b < 1) return fail(QSVD_ERR_INVALID, "decode: b = %d < 1", b);
+  if (L < 1) return fail(QSVD_ERR_INVALID, "decode: L = %lld < 1", (long long)L);
+  if (heads < 1 || heads > 256) return fail(QSVD_ERR_INVALID, "decode: heads = %d (1..256)", heads);
+  if (d != 16 && d != 32 && d != 64 && d != 128 && d != 256)
+    return fail(QSVD_ERR_UNSUPPORTED, "decode: d = %d (16, 32, 64, 128 or 256)", d);
+  if (splits < 0) return fail(QSVD_ERR_INVALID, "decode: splits = %d < 0", splits);
+  if (c_dtype == QSVD_F32) {
+    if (r < 1 || r > 4096) return fail(QSVD_ERR_UNSUPPORTED, "decode: F32 cache needs 1 <= r <= 4096");
+  } else if (c_dtype == QSVD_BF16 || c_dtype == QSVD_I8 || c_dtype == QSVD_I4) {
+    if (r < 32 || r % 32 != 0)
+      return fail(QSVD_ERR_INVALID, "decode: r = %d must be a positive multiple of 32", r);
+    if (c_dtype == QSVD_I4 && r % 128 != 0)
+      return fail(QSVD_ERR_INVALID, "decode: int4 cache needs r %% 128 == 0 (r = %d)", r);
+    int W = 1;
+    for (int w : {8, 4, 2, 1})
+      if (r % (32 * w) == 0) {
+        W = w;
+        break;
+      }
+    if (r / W / 16 > 18)
+      return fail(QSVD_ERR_UNSUPPORTED, "decode: r = %d exceeds the per-wavefront column budget", r);
+  } else {
+    return fail(QSVD_ERR_INVALID, "decode: c_dtype %s", dtype_name(c_dtype));
+  }
+  if (static_cast<int64_t>(b) * L > (int64_t(1) << 40))
+    return fail(QSVD_ERR_INVALID, "decode: b * L too large");
+  return QSVD_OK;
+}
+
+size_t qsvd_decode_workspace_bytes(int32_t b, int64_t L, int32_t r, int32_t heads, int32_t d,
+                                   qsvd_dtype_t c_dtype, int32_t splits) {
+  if (validate_decode_shape(b, L, r, heads, d, c_dtype, splits) != QSVD_OK) return 0;
+  return qsvd::plan_decode(b, L, r, heads, d, c_dtype, splits).total;
+}
+
+int32_t qsvd_decode_default_splits(int32_t b, int64_t L, int32_t r, int32_t heads, int32_t d,
+                                   qsvd_dtype_t c_dtype) {
+  if (validate_decode_shape(b, L, r, heads, d, c_dtype, 0) != QSVD_OK) return 0;
+  return qsvd::plan_decode(b, L, r, heads, d, c_dtype, 0).splits;
+}
+
+qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                               qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
+                               const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
+                               const float *wu_scale_k, const float *wu_scale_v, int32_t b,
+                               int64_t L, int32_t r, int32_t heads, int32_t d,
+                               float softmax_scale, int32_t splits, void *O, qsvd_dtype_t o_dtype,
+                               void *workspace, size_t workspace_bytes, void *hip_stream) {
+  qsvd_status_t st = validate_decode_shape(b, L, r, heads, d, c_dtype, splits);
+  if (st != QSVD_OK) return st;
+  if (c_dtype == QSVD_F32) {
+    if (q_dtype != QSVD_F32 || wu_dtype != QSVD_F32 || o_dtype != QSVD_F32)
+      return fail(QSVD_ERR_UNSUPPORTED, "decode: F32 cache needs F32 q, W^u and O");
+  } else {
+    if (q_dtype != QSVD_BF16)
+      return fail(QSVD_ERR_UNSUPPORTED, "decode: %s cache needs BF16 q", dtype_name(c_dtype));
+    if (wu_dtype != QSVD_BF16 && wu_dtype != QSVD_I8)
+      return fail(QSVD_ERR_UNSUPPORTED, "decode: W^u dtype %s (BF16 or I8)", dtype_name(wu_dtype));
+    if (o_dtype != QSVD_BF16 && o_dtype != QSVD_F32)
+      return fail(QSVD_ERR_INVALID, "decode: o_dtype %s", dtype_name(o_dtype));
+  }
+  if (c_dtype == QSVD_I4) {
+    if (c_group != 128) return fail(QSVD_ERR_UNSUPPORTED, "decode: int4 cache needs c_group 128");
+    if (!c_scales) return fail(QSVD_ERR_INVALID, "decode: int4 cache needs c_scales");
+  } else if (c_dtype == QSVD_I8) {
+    if (c_group != 0) return fail(QSVD_ERR_UNSUPPORTED, "decode: int8 cache is per token (c_group 0)");
+    if (!c_scales) return fail(QSVD_ERR_INVALID, "decode: int8 cache needs c_scales");
+  } else {
+    if (c_scales || c_group != 0)
+      return fail(QSVD_ERR_INVALID, "decode: %s cache takes no scales", dtype_name(c_dtype));
+  }
+  if (wu_dtype == QSVD_I8) {
+    if (!wu_scale_k || !wu_scale_v)
+      return fail(QSVD_ERR_INVALID, "decode: int8 W^u needs wu_scale_k and wu_scale_v");
+  } else if (wu_scale_k || wu_scale_v) {
+    return fail(QSVD_ERR_INVALID, "decode: %s W^u takes no scales", dtype_name(wu_dtype));
+  }
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
+    return fail(QSVD_ERR_INVALID, "decode: softmax_scale must be positive and finite");
+  if (!q || !C || !Wu_k || !Wu_v || !O) return fail(QSVD_ERR_INVALID, "decode: NULL pointer");
+  if (!aligned16(q) || !aligned16(C) || !aligned16(Wu_k) || !aligned16(Wu_v) || !aligned16(O) ||
+      (c_scales && !aligned4(c_scales)) || (workspace && !aligned16(workspace)))
+    return fail(QSVD_ERR_INVALID, "decode: misaligned pointer");
+  const qsvd::DecodePlan plan = qsvd::plan_decode(b, L, r, heads, d, c_dtype, splits);
+  if (!workspace || workspace_bytes < plan.total)
+    return fail(QSVD_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
+                plan.total);
+  qsvd::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.C = C;
+  a.c_dtype = c_dtype;
+  a.c_scales = c_scales;
+  a.c_group = c_group;
+  a.Wu_k = Wu_k;
+  a.Wu_v = Wu_v;
+  a.wu_dtype = wu_dtype;
+  a.wu_scale_k = wu_scale_k;
+  a.wu_scale_v = wu_scale_v;
+  a.b = b;
+  a.L = L;
+  a.r = r;
+  a.heads = heads;
+  a.d = d;
+  a.softmax_scale = softmax_scale;
+  a.splits = splits;
+  a.O = O;
+  a.o_dtype = o_dtype;
+  a.workspace = workspace;
+  return device_status(qsvd::launch_decode(a, plan, static_cast<hipStream_t>(hip_stream)),
+                       "decode_attn");
+}
+
+qsvd_status_t qsvd_timing_begin(int32_t max_launches) {
+  TimingSession &t = g_timing;
+  if (t.active) return fail(QSVD_ERR_INVALID, "timing_begin: a session is already active");
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(QSVD_ERR_INVALID, "timing_begin: max_launches = %d", max_launches);
+  t.pool.resize(static_cast<size_t>(2) * max_launches);
+  for (auto &ev : t.pool) {
+    const hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return device_status(e, "timing_begin");
+  }
+  t.records.clear();
+  t.records.reserve(max_launches);
+  t.max_launches = max_launches;
+  t.active = true;
+  return ok();
+}
+
+qsvd_status_t qsvd_timing_end(qsvd_kernel_time_t *out, int32_t max_out, int32_t *n_out) {
+  TimingSession &t = g_timing;
+  if (!t.active) return fail(QSVD_ERR_INVALID, "timing_end: no active session");
+  t.active = false;
+  hipError_t err = hipSuccess;
+  std::vector<qsvd_kernel_time_t> agg;
+  if (!t.records.empty()) err = hipEventSynchronize(t.records.back().stop);
+  for (const auto &rec : t.records) {
+    if (err != hipSuccess) break;
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, rec.start, rec.stop);
+    if (err != hipSuccess) break;
+    qsvd_kernel_time_t *slot = nullptr;
+    for (auto &a : agg)
+      if (std::strncmp(a.name, rec.name, sizeof(a.name)) == 0) slot = &a;
+    if (!slot) {
+      qsvd_kernel_time_t k{};
+      std::strncpy(k.name, rec.name, sizeof(k.name) - 1);
+      agg.push_back(k);
+      slot = &agg.back();
+    }
+    slot->launches += 1;
+    slot->total_ms += ms;
+  }
+  for (auto &ev : t.pool) (void)hipEventDestroy(ev);
+  t.pool.clear();
+  t.records.clear();
+  if (err != hipSuccess) return device_status(err, "timing_end");
+  const int n = static_cast<int>(agg.size());
+  if (n_out) *n_out = n;
+  for (int i = 0; i < n && i < max_out && out; ++i) out[i] = agg[i];
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "qsvd.h"
+
+namespace qsvd {
+
+// ---------------------------------------------------------------- timing
+// RAII bracket around one kernel launch: records a HIP event pair on the
+// launch stream when a timing session is active on this thread.
+class LaunchTimer {
+ public:
+  LaunchTimer(const char *name, hipStream_t stream);
+  ~LaunchTimer();
+  LaunchTimer(const LaunchTimer &) = delete;
+  LaunchTimer &operator=(const LaunchTimer &) = delete;
+
+ private:
+  int slot_;
+  hipStream_t stream_;
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns the HIP error of its launches (hipSuccess on success).  All
+// shapes are validated by the caller.
+
+hipError_t launch_rotate_quant(const void *in, bool in_bf16, int64_t M, int n, bool hadamard,
+                               bool int4, bool grouped, void *codes, float *scales,
+                               hipStream_t s);
+
+hipError_t launch_gemm(const void *A, const float *a_scale, bool int8, int64_t M, int K,
+                       const void *Bt, const float *col_scale, int N, void *C, bool c_bf16,
+                       hipStream_t s);
+
+hipError_t launch_transpose(const void *W, int elem_bytes, int rows, int cols, void *out,
+                            hipStream_t s);
+
+struct DecodeArgs {
+  const void *q;
+  int q_dtype;
+  const void *C;
+  int c_dtype;
+  const float *c_scales;
+  int c_group;
+  const void *Wu_k;
+  const void *Wu_v;
+  int wu_dtype;
+  const float *wu_scale_k;
+  const float *wu_scale_v;
+  int b;
+  int64_t L;
+  int r;
+  int heads;
+  int d;
+  float softmax_scale;
+  int splits;
+  void *O;
+  int o_dtype;
+  void *workspace;
+};
+
+// Workspace layout of one decode call.
+struct DecodePlan {
+  int splits;        // L-splits per sequence
+  int64_t chunk;     // tokens per split (multiple of the token tile)
+  int head_groups;   // workgroups per (sequence, split) along heads
+  int group_heads;   // heads per head group
+  bool mfma;         // bf16 / quantised MFMA stream kernel (else float32 kernel)
+  size_t qt_bytes;   // absorbed queries
+  size_t part_bytes; // per-split partial state
+  size_t total;
+};
+
+DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, int splits);
+
+hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s);
+
+}  // namespace qsvd

@@ -1,0 +1,83 @@
+"""Helpers for the GPU parity tests: host <-> device copies and one-call wrappers
+around the C ABI (through the Python binding)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import rank_latent_attention_amd as q
+
+DEV = "cuda"
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray):
+    """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t) -> np.ndarray:
+    """device tensor -> numpy (bf16 -> float64 values; float32 -> float64)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def bf16_bits(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def empty(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=DEV)
+
+
+def workspace(nbytes: int):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=DEV)
+
+
+def decode(qv, q_dtype, C, c_dtype, Wk, Wv, wu_dtype, b, L, r, heads, d, scale, *,
+           c_scales=None, c_group=0, wsk=None, wsv=None, splits=0, o_dtype=None):
+    """Run qsvd_decode_attn on device tensors; returns the output tensor."""
+    import torch
+    if o_dtype is None:
+        o_dtype = q.F32 if c_dtype == q.F32 else q.BF16
+    O = empty((b, heads, d), torch.float32 if o_dtype == q.F32 else torch.bfloat16)
+    nbytes = q.qsvd_decode_workspace_bytes(b, L, r, heads, d, c_dtype, splits)
+    assert nbytes > 0
+    ws = workspace(nbytes)
+    q.qsvd_decode_attn(qv, q_dtype, C, c_dtype, c_scales, c_group, Wk, Wv, wu_dtype, wsk, wsv,
+                       b, L, r, heads, d, scale, splits, O, o_dtype, ws)
+    torch.cuda.synchronize()
+    return O
+
+
+def decode_case_on_gpu(cs, splits=0, o_dtype=None, q_override=None):
+    """Decode a synth.DecodeCase (float32 or bf16 storage) on the GPU."""
+    dt = q.F32 if cs.dtype == "f32" else q.BF16
+    qv = dev(cs.q if q_override is None else q_override)
+    O = decode(qv, dt, dev(cs.C), dt, dev(cs.Wu_k), dev(cs.Wu_v), dt, cs.b, cs.L, cs.r, cs.heads,
+               cs.d, cs.softmax_scale, splits=splits, o_dtype=o_dtype)
+    return host(O)
+
+
+def values(cs_array, dtype: str) -> np.ndarray:
+    """Exact float64 values of a stored input (float32 or bf16 bits)."""
+    import oracle
+    if dtype == "bf16":
+        return oracle.bf16_decode(cs_array)
+    return np.asarray(cs_array, np.float64)

@@ -1,0 +1,151 @@
+"""The C-ABI library loads on the CPU, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call.  No kernel is launched:
+every call below fails validation (or is a pure query)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rank_latent_attention_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsvd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q.library_path),
+                                reason="libqsvd.so not built (run __graft_entry__.build())")
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsvd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = q.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", q.library_path], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (qsvd_\w+)", out))
+    assert set(names) <= exported
+    assert set(q.EXPORTED) == set(names)
+
+
+def test_status_strings():
+    assert q.qsvd_status_string(0) == "QSVD_OK"
+    for s in (-1, -2, -3, -4):
+        assert q.qsvd_status_string(s).startswith("QSVD_ERR")
+
+
+def st_quant(**kw):
+    a = dict(inp=FAKE, in_dtype=q.F32, M=4, n=256, had=128, code=q.I8, group=0, codes=FAKE,
+             scales=FAKE)
+    a.update(kw)
+    return q.lib().qsvd_quantize_latent(a["inp"], a["in_dtype"], a["M"], a["n"], a["had"],
+                                        a["code"], a["group"], a["codes"], a["scales"], None)
+
+
+def test_quantize_validation():
+    assert st_quant(in_dtype=q.I8) == -1
+    assert st_quant(code=q.BF16) == -1
+    assert st_quant(had=64) == -2
+    assert st_quant(group=64) == -2
+    assert st_quant(n=100, had=0) == -1          # n % 8
+    assert st_quant(n=264, had=128) == -1        # n % 128 with rotation
+    assert st_quant(n=264, had=0, group=128) == -1
+    assert st_quant(n=16384) == -1               # > 8192
+    assert st_quant(M=-1) == -1
+    assert st_quant(inp=None) == -1
+    assert st_quant(codes=ctypes.c_void_p((1 << 20) + 8)) == -1   # misaligned
+    assert "misaligned" in q.qsvd_last_error()
+    assert st_quant(M=0, inp=None) == 0          # empty: no-op, no launch
+
+
+def st_proj(**kw):
+    a = dict(X=FAKE, xdt=q.I8, xs=FAKE, M=16, E=256, W=FAKE, wdt=q.I8, cs=None, r=64, C=FAKE,
+             cdt=q.F32)
+    a.update(kw)
+    return q.lib().qsvd_project(a["X"], a["xdt"], a["xs"], a["M"], a["E"], a["W"], a["wdt"],
+                                a["cs"], a["r"], a["C"], a["cdt"], None)
+
+
+def test_project_validation():
+    assert st_proj(xdt=q.F32, wdt=q.F32) == -2
+    assert st_proj(wdt=q.BF16) == -2
+    assert st_proj(cdt=q.I8) == -1
+    assert st_proj(E=100) == -1
+    assert st_proj(r=40) == -1
+    assert st_proj(xs=None) == -1                # int8 needs per-token scales
+    assert st_proj(xdt=q.BF16, wdt=q.BF16) == -1  # bf16 takes no x_scale
+    assert st_proj(M=-5) == -1
+    assert st_proj(C=None) == -1
+    assert st_proj(M=0, X=None) == 0
+
+
+def st_dec(**kw):
+    a = dict(q_=FAKE, qdt=q.BF16, C=FAKE, cdt=q.BF16, cs=None, cg=0, Wk=FAKE, Wv=FAKE,
+             wdt=q.BF16, wsk=None, wsv=None, b=2, L=100, r=256, heads=4, d=64, scale=0.125,
+             splits=0, O=FAKE, odt=q.BF16, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return q.lib().qsvd_decode_attn(a["q_"], a["qdt"], a["C"], a["cdt"], a["cs"], a["cg"], a["Wk"],
+                                    a["Wv"], a["wdt"], a["wsk"], a["wsv"], a["b"], a["L"], a["r"],
+                                    a["heads"], a["d"], a["scale"], a["splits"], a["O"], a["odt"],
+                                    a["ws"], a["wsb"], None)
+
+
+def test_decode_validation():
+    assert st_dec(b=0) == -1
+    assert st_dec(L=0) == -1
+    assert st_dec(d=48) == -2
+    assert st_dec(r=100) == -1                    # bf16 cache needs r % 32
+    assert st_dec(r=4096) == -2                   # beyond the per-wavefront budget
+    assert st_dec(cdt=q.I4, cs=FAKE, cg=128, r=96) == -1   # int4 needs r % 128
+    assert st_dec(cdt=q.I4, cs=FAKE, cg=0) == -2
+    assert st_dec(cdt=q.I4, cs=None, cg=128) == -1
+    assert st_dec(cdt=q.I8, cs=FAKE, cg=128) == -2
+    assert st_dec(cs=FAKE) == -1                  # bf16 cache takes no scales
+    assert st_dec(qdt=q.F32) == -2
+    assert st_dec(wdt=q.F32) == -2
+    assert st_dec(wdt=q.I8) == -1                 # int8 W^u needs column scales
+    assert st_dec(wsk=FAKE, wsv=FAKE) == -1       # bf16 W^u takes none
+    assert st_dec(cdt=q.F32, qdt=q.F32, wdt=q.F32, odt=q.BF16) == -2
+    assert st_dec(scale=0.0) == -1
+    assert st_dec(scale=float("nan")) == -1
+    assert st_dec(splits=-1) == -1
+    assert st_dec(O=None) == -1
+    assert st_dec(ws=ctypes.c_void_p((1 << 20) + 4)) == -1
+    need = q.qsvd_decode_workspace_bytes(2, 100, 256, 4, 64, q.BF16)
+    assert need > 0
+    assert st_dec(wsb=need - 1) == -3
+    assert st_dec(ws=None) == -3
+    assert "workspace" in q.qsvd_last_error()
+
+
+def test_workspace_and_splits_plan():
+    # the default split count fills the 256 compute units once
+    assert q.qsvd_decode_default_splits(16, 8192, 1536, 32, 128, q.BF16) * 16 * 2 <= 256
+    assert q.qsvd_decode_default_splits(8, 16384, 2304, 40, 128, q.BF16) == 10
+    assert q.qsvd_decode_default_splits(1, 5, 256, 4, 64, q.BF16) == 1
+    w1 = q.qsvd_decode_workspace_bytes(16, 8192, 1536, 32, 128, q.BF16, 1)
+    w8 = q.qsvd_decode_workspace_bytes(16, 8192, 1536, 32, 128, q.BF16, 8)
+    assert 0 < w1 < w8
+    # partial state grows with the split count: heads * r * 2 bytes per split
+    assert w8 - w1 >= 7 * 16 * 32 * 1536 * 2
+    assert q.qsvd_decode_workspace_bytes(16, 8192, 1536, 32, 100, q.BF16) == 0   # invalid shape
+    # explicit split counts are honoured up to one token per split
+    assert q.qsvd_decode_workspace_bytes(1, 3, 256, 4, 64, q.BF16, 64) == \
+        q.qsvd_decode_workspace_bytes(1, 3, 256, 4, 64, q.BF16, 3)
+
+
+def test_timing_session_errors():
+    L = q.lib()
+    n = ctypes.c_int32(0)
+    assert L.qsvd_timing_end(None, 0, ctypes.byref(n)) == -1
+    assert L.qsvd_timing_begin(0) == -1

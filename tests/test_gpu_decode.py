@@ -1,0 +1,182 @@
+"""GPU parity of qsvd_decode_attn against the float64 oracle (explicit K and V).
+
+Tolerances: relative L2 over the whole [b][heads][d] output, 1e-5 for the
+float32 path and 2e-2 for bf16 and quantised caches.  The oracle consumes the
+exact stored values (float32, bf16 or code x scale), so the tolerance covers
+only the kernel's own rounding: bf16 absorbed queries, bf16 probabilities,
+bf16 split partials and the bf16 output (each <= 2^-9 relative).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bf16_bits, decode, decode_case_on_gpu, dev, host, say, values
+
+import rank_latent_attention_amd as q
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def oracle_out(cs, qv=None):
+    qq = values(cs.q, cs.dtype) if qv is None else qv
+    return oracle.attend_explicit(qq, values(cs.C, cs.dtype), values(cs.Wu_k, cs.dtype),
+                                  values(cs.Wu_v, cs.dtype), cs.heads, cs.d, cs.softmax_scale)
+
+
+# ------------------------------------------------------------------ float32 path
+def test_tiny_fp32_config():
+    cfg = synth.CONFIGS[0]
+    say(f"case: {cfg.name}")
+    cs = synth.config_decode_case(cfg)
+    got = decode_case_on_gpu(cs)
+    err = oracle.rel_l2(got, oracle_out(cs))
+    say(f"  rel-L2 {err:.2e}")
+    assert err <= TOL_F32
+
+
+def test_fact_a_on_gpu_full_rank_matches_original_attention():
+    """r = E without quantisation: the GPU latent path equals attention with the
+    original W_Q, W_K, W_V (QSVD notes, 'Key design'), computed by the oracle."""
+    E, heads, d, L = 256, 4, 64, 512
+    say("case: fact (a) E=256 r=256 fp32")
+    cs = synth.decode_case(E, heads, d, E, 1, L, dtype="f32", seed=1000, keep_x=True, k=E)
+    got = decode_case_on_gpu(cs)
+    Wc = cs.layer.W_concat()
+    X = cs.X[0]
+    ref = oracle.attend_original(X[:L], X[L], Wc[:, :E], Wc[:, E:2 * E], Wc[:, 2 * E:], heads, d)
+    err = oracle.rel_l2(got[0], ref)
+    say(f"  rel-L2 vs original attention {err:.2e}")
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("L", [1, 17, 513])
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 10 ** 6])
+def test_fp32_split_invariance(L, splits):
+    say(f"case: fp32 L={L} splits={splits}")
+    cs = synth.decode_case(256, 4, 64, 96, 2, L, dtype="f32", seed=31)
+    got = decode_case_on_gpu(cs, splits=min(splits, 1024))
+    assert oracle.rel_l2(got, oracle_out(cs)) <= TOL_F32
+
+
+# ------------------------------------------------------------------ bf16 path
+BF16_SHAPES = [
+    # E, heads, d, r, b, L
+    (256, 4, 64, 128, 2, 1),
+    (256, 4, 64, 256, 3, 17),
+    (512, 4, 128, 768, 2, 300),
+    (1024, 16, 64, 512, 2, 1000),
+    (2048, 16, 128, 2304, 1, 77),
+    (4096, 32, 128, 1536, 2, 700),
+    (5120, 40, 128, 2304, 1, 333),
+    (768, 6, 128, 96, 2, 65),
+]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: "E{}h{}d{}r{}b{}L{}".format(*s))
+def test_bf16_shapes(shape):
+    E, heads, d, r, b, L = shape
+    say(f"case: bf16 {shape}")
+    cs = synth.decode_case(E, heads, d, r, b, L, dtype="bf16", hadamard=128 if r % 128 == 0 else 0,
+                           p=0.5, outlier_gain=50.0, seed=100 + r)
+    got = decode_case_on_gpu(cs)
+    err = oracle.rel_l2(got, oracle_out(cs))
+    say(f"  rel-L2 {err:.2e}")
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("factor", [1.0, 30.0, 300.0])
+def test_bf16_sharpened_softmax(factor):
+    """Sharpened queries (score spread of several units) exercise the online
+    rescaling across tiles and the split merge; near-uniform attention would not."""
+    say(f"case: bf16 sharpened x{factor}")
+    cs = synth.decode_case(1024, 8, 128, 512, 2, 900, dtype="bf16", hadamard=128, p=0.5, seed=77)
+    qv = synth.to_bf16_bits(synth.sharpen_query(values(cs.q, "bf16"), factor))
+    ref = oracle_out(cs, qv=values(qv, "bf16"))
+    for splits in (1, 3, 0):
+        got = decode_case_on_gpu(cs, splits=splits, q_override=qv)
+        err = oracle.rel_l2(got, ref)
+        say(f"  splits={splits} rel-L2 {err:.2e}")
+        assert err <= TOL_BF16
+
+
+def test_bf16_split_invariance_and_determinism():
+    say("case: bf16 split invariance")
+    cs = synth.decode_case(512, 4, 128, 256, 2, 8191 // 8, dtype="bf16", hadamard=128, seed=5)
+    ref = oracle_out(cs)
+    for splits in (1, 2, 7, 64, 1024):
+        got = decode_case_on_gpu(cs, splits=splits)
+        assert oracle.rel_l2(got, ref) <= TOL_BF16, splits
+    # bitwise repeatable at a fixed split count
+    a = decode_case_on_gpu(cs, splits=7)
+    b = decode_case_on_gpu(cs, splits=7)
+    assert np.array_equal(a, b)
+
+
+def test_bf16_float32_output():
+    cs = synth.decode_case(512, 4, 128, 256, 2, 100, dtype="bf16", hadamard=128, seed=9)
+    got = decode_case_on_gpu(cs, o_dtype=q.F32)
+    assert oracle.rel_l2(got, oracle_out(cs)) <= TOL_BF16
+
+
+# ------------------------------------------------------------------ quantised caches
+def _quant_case(r, L, b, heads, d, bits, seed):
+    g = np.random.default_rng(seed)
+    E = heads * d
+    qmax = 7 if bits == 4 else 127
+    codes = g.integers(-qmax, qmax + 1, size=(b, L, r)).astype(np.int8)
+    if bits == 4:
+        scales = (g.random((b, L, r // 128)) * 0.05 + 0.01).astype(np.float32)
+    else:
+        scales = (g.random((b, L)) * 0.01 + 0.001).astype(np.float32)
+    Wk = g.standard_normal((r, E)) / math.sqrt(r)
+    Wv = g.standard_normal((r, E)) / math.sqrt(r)
+    Wk_q, Wk_s = synth.int8_columns(Wk)
+    Wv_q, Wv_s = synth.int8_columns(Wv)
+    qv = synth.to_bf16_bits(g.standard_normal((b, heads, d)) * 2.0)
+    return codes, scales, Wk_q, Wk_s, Wv_q, Wv_s, qv
+
+
+@pytest.mark.parametrize("bits,r,L,b,heads", [(4, 768, 1000, 2, 32), (4, 128, 5, 1, 4),
+                                               (8, 512, 333, 2, 16), (4, 2304, 200, 1, 40)])
+@pytest.mark.parametrize("wu", ["i8", "bf16"])
+def test_quantised_cache(bits, r, L, b, heads, wu):
+    d = 128
+    say(f"case: int{bits} cache r={r} L={L} b={b} heads={heads} W^u {wu}")
+    codes, scales, Wk_q, Wk_s, Wv_q, Wv_s, qv = _quant_case(r, L, b, heads, d, bits, seed=r + L)
+    group = 128 if bits == 4 else 0
+    Chat = oracle.dequant_rows(codes, scales, group)
+    if wu == "i8":
+        Wk = oracle.dequant_cols(Wk_q, Wk_s)
+        Wv = oracle.dequant_cols(Wv_q, Wv_s)
+        Wk_d, Wv_d, wdt = dev(Wk_q), dev(Wv_q), q.I8
+        wsk, wsv = dev(Wk_s), dev(Wv_s)
+    else:
+        Wk_b = synth.to_bf16_bits(oracle.dequant_cols(Wk_q, Wk_s))
+        Wv_b = synth.to_bf16_bits(oracle.dequant_cols(Wv_q, Wv_s))
+        Wk, Wv = oracle.bf16_decode(Wk_b), oracle.bf16_decode(Wv_b)
+        Wk_d, Wv_d, wdt, wsk, wsv = dev(Wk_b), dev(Wv_b), q.BF16, None, None
+    C_dev = dev(oracle.pack_int4(codes)) if bits == 4 else dev(codes)
+    cdt = q.I4 if bits == 4 else q.I8
+    ref = oracle.attend_explicit(oracle.bf16_decode(qv), Chat, Wk, Wv, heads, d, 1 / math.sqrt(d))
+    for splits in (0, 3):
+        O = decode(dev(qv), q.BF16, C_dev, cdt, Wk_d, Wv_d, wdt, b, L, r, heads, d,
+                   1 / math.sqrt(d), c_scales=dev(scales), c_group=group, wsk=wsk, wsv=wsv,
+                   splits=splits)
+        err = oracle.rel_l2(host(O), ref)
+        say(f"  splits={splits} rel-L2 {err:.2e}")
+        assert err <= TOL_BF16
+
+
+def test_output_unchanged_by_rotation_on_gpu():
+    """Fact (b) through the GPU: the same layer with H2 = WHT-128 folded into the
+    cache and W^u, or with H2 = I, gives the same attention (bf16 tolerance)."""
+    a = synth.decode_case(1024, 8, 128, 512, 2, 256, dtype="bf16", hadamard=128, seed=3)
+    b = synth.decode_case(1024, 8, 128, 512, 2, 256, dtype="bf16", hadamard=0, seed=3)
+    ga, gb = decode_case_on_gpu(a), decode_case_on_gpu(b)
+    assert oracle.rel_l2(ga, gb) <= TOL_BF16
