@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSVD latent-attention hot path on one MI355X.
+
+Decode leg (the headline): one decode step of a LLaVA-v1.5-7B-shaped joint-QKV
+latent-attention layer, E = 4096 (32 heads x 128), r = 1536, b = 16 sequences,
+L = 8192 cached bf16 latents each; the step is qsvd_decode_attn (absorb,
+split-L stream, merge, finalize).  value = decode tokens/s = b / step time.
+
+Prefill leg: the shared down-projection at W8A8, X [16384][4096] int8 (H1
+rotated, per-token scales) times W^d [4096][1536] int8 (per-column scales),
+reported as TOPS; plus the rotate+quantise steps around it.
+
+All inputs are seeded synthetic data (synth/); the cache copies are rotated
+between steps so that the 256 MiB last-level cache cannot serve a step from
+the previous one.  Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+COUNTERS = os.path.join(ROOT, "profiles", "decode_stream_e4096_r1536_b16_l8192_counters.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=2, help="rotated cache copies")
+    ap.add_argument("--splits", type=int, default=0, help="L-splits (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--chain", action="store_true", help="also time the 24-layer prefill chain")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "rank_latent_attention_amd", "csrc", "decode.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the latent-attention "
+              "decode shards by sequence with no communication, so N GPUs run N independent "
+              "copies of this single-GPU step.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_latent_attention_amd as q
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    bf = lambda u16: dev(u16.view(np.int16)).view(torch.bfloat16)
+
+    # ------------------------------------------------------------------ decode
+    cfg = synth.CONFIGS[1]
+    b, L, r, heads, d = cfg.b, cfg.L, cfg.r, cfg.heads, cfg.d
+    t0 = time.time()
+    cs = synth.config_decode_case(cfg)
+    log(f"[bench] generated decode inputs ({cfg.name}) in {time.time() - t0:.1f}s")
+    C0 = bf(cs.C)
+    copies = [C0] + [C0.clone() for _ in range(max(args.copies, 1) - 1)]
+    qv, Wk, Wv = bf(cs.q), bf(cs.Wu_k), bf(cs.Wu_v)
+    O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = q.qsvd_decode_workspace_bytes(b, L, r, heads, d, q.BF16, args.splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    splits = args.splits or q.qsvd_decode_default_splits(b, L, r, heads, d, q.BF16)
+
+    def step(i):
+        q.qsvd_decode_attn(qv, q.BF16, copies[i % len(copies)], q.BF16, None, 0, Wk, Wv, q.BF16,
+                           None, None, b, L, r, heads, d, cs.softmax_scale, args.splits, O,
+                           q.BF16, ws, ws_bytes)
+
+    ms = timed(step, args.steps, args.warmup)
+    # per-kernel HIP-event times over a second pass of the same steps
+    with q.timing(max_launches=8 * args.steps + 16) as tm:
+        for i in range(args.steps):
+            step(i)
+    torch.cuda.synchronize()
+    kern = {k: v[1] / v[0] for k, v in tm.result.items()}
+    log(f"[bench] decode step {ms * 1e3:.1f} us; kernels (us): " +
+        ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kern.items()))
+
+    # sampled parity of the timed output (sequence 0, four heads)
+    import oracle
+    got = O.float().cpu().numpy()[0, :4]
+    v = oracle.bf16_decode
+    ref = oracle.attend_explicit_heads(v(cs.q[0]), v(cs.C[0]), v(cs.Wu_k), v(cs.Wu_v), range(4), d,
+                                       cs.softmax_scale)
+    parity = oracle.rel_l2(got, ref)
+
+    cache_bytes = b * L * r * 2                       # one r-wide bf16 latent per cached token
+    step_bytes = cache_bytes + 2 * r * heads * d * 2 + 2 * b * heads * d * 2
+    stream_ms = kern.get("decode_stream", float("nan"))
+    achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        if c.get("decode_hip_sha256_16") == kernel_source_hash():
+            traffic = c.get("hbm_bytes_per_launch")
+
+    # ------------------------------------------------------------------ prefill
+    prefill = None
+    if not args.no_prefill:
+        M, E, rp = 4 * 4096, 4096, 1536
+        t0 = time.time()
+        X = synth.to_bf16_bits(synth.prefill_activations(M, E))
+        Wd_q, Wd_s = synth.down_projection_int8(E, rp, 0.5, 0.5, 128, (100400,))
+        log(f"[bench] generated prefill inputs in {time.time() - t0:.1f}s")
+        Xd = bf(X)
+        del X
+        Wt = dev(np.ascontiguousarray(Wd_q.T))
+        ws_d = dev(Wd_s)
+        xq = torch.empty((M, E), dtype=torch.int8, device="cuda")
+        xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+        Cp = torch.empty((M, rp), dtype=torch.float32, device="cuda")
+        cq = torch.empty((M, rp), dtype=torch.int8, device="cuda")
+        csc = torch.empty((M,), dtype=torch.float32, device="cuda")
+        a1 = lambda i: q.qsvd_quantize_latent(Xd, q.BF16, M, E, 128, q.I8, 0, xq, xs)
+        a2 = lambda i: q.qsvd_project(xq, q.I8, xs, M, E, Wt, q.I8, ws_d, rp, Cp, q.F32)
+        a3 = lambda i: q.qsvd_quantize_latent(Cp, q.F32, M, rp, 128, q.I8, 0, cq, csc)
+        steps = max(args.steps // 2, 5)
+        t_a1 = timed(a1, steps, 3)
+        t_a2 = timed(a2, steps, 3)
+        t_a3 = timed(a3, steps, 3)
+        tops = 2.0 * M * E * rp / (t_a2 * 1e-3) / 1e12
+        prefill = {"workload": "X[16384][4096] int8 x W^d[4096][1536] int8 -> fp32",
+                   "proj_us": round(t_a2 * 1e3, 2), "proj_tops": round(tops, 1),
+                   "peak_tops": INT8_PEAK_TOPS, "frac": round(tops / INT8_PEAK_TOPS, 4),
+                   "rotate_quant_x_us": round(t_a1 * 1e3, 2),
+                   "rotate_quant_c_us": round(t_a3 * 1e3, 2)}
+        log(f"[bench] prefill: a1 {t_a1 * 1e3:.1f} us, a2 {t_a2 * 1e3:.1f} us ({tops:.0f} TOPS), "
+            f"a3 {t_a3 * 1e3:.1f} us")
+        if args.chain:
+            prefill["chain"] = chain_leg(q, torch, np, synth, xq, xs, M, E, steps=3)
+        del Xd, xq, Cp, cq
+
+    # ------------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cs, oracle)
+
+    out = {
+        "metric": "decode tokens/s + HBM GB/s (E=4096,r=1536,b=16,L=8192); prefill proj TOPS",
+        "value": round(b / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "latent-attention decode step, E=4096 (32x128), r=1536, b=16, "
+                               "L=8192, bf16 latent cache (LLaVA-v1.5-7B shape)",
+                   "global_batch": b, "seq_len": L, "rank": r, "splits": splits,
+                   "cache_copies": len(copies)},
+        "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": "decode_stream", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": cache_bytes},
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+        "parity_rel_l2_sample": float(f"{parity:.3e}"),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def chain_leg(q, torch, np, synth, xq, xs, M, E, steps):
+    """24 layers: projection to r_l, H2 rotate + int8 requantise, K/V rebuild (int8 GEMM to
+    2E columns, bf16 out).  Timing-only weights: seeded int8 codes with unit scales."""
+    ranks = synth.c4_ranks()
+    g = np.random.default_rng(7)
+    layers = []
+    for rl in ranks:
+        Wd = dev_t(torch, np, g.integers(-127, 128, size=(int(rl), E)).astype(np.int8))
+        Wkv = dev_t(torch, np, g.integers(-127, 128, size=(2 * E, int(rl))).astype(np.int8))
+        sd = torch.full((int(rl),), 1e-3, device="cuda")
+        skv = torch.full((2 * E,), 1e-3, device="cuda")
+        layers.append((int(rl), Wd, sd, Wkv, skv))
+    rmax = int(max(ranks))
+    Cp = torch.empty((M, rmax), dtype=torch.float32, device="cuda")
+    cq = torch.empty((M, rmax), dtype=torch.int8, device="cuda")
+    csc = torch.empty((M,), dtype=torch.float32, device="cuda")
+    KV = torch.empty((M, 2 * E), dtype=torch.bfloat16, device="cuda")
+
+    def run(_):
+        for rl, Wd, sd, Wkv, skv in layers:
+            q.qsvd_project(xq, q.I8, xs, M, E, Wd, q.I8, sd, rl, Cp, q.F32)
+            q.qsvd_quantize_latent(Cp, q.F32, M, rl, 128, q.I8, 0, cq, csc)
+            q.qsvd_project(cq, q.I8, csc, M, rl, Wkv, q.I8, skv, 2 * E, KV, q.BF16)
+
+    ms = timed(run, steps, 1)
+    ops = sum(2.0 * M * E * rl + 2.0 * M * rl * 2 * E for rl in ranks)
+    return {"layers": len(ranks), "ms": round(ms, 3), "tops": round(ops / (ms * 1e-3) / 1e12, 1)}
+
+
+def dev_t(torch, np, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cpu_baseline(cs, oracle):
+    """The float64 oracle (explicit K and V) on whole sequences of the same decode step,
+    one sequence at a time until about 10 s of CPU work."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    v = oracle.bf16_decode
+    Wk, Wv = v(cs.Wu_k), v(cs.Wu_v)
+    n, t0 = 0, time.perf_counter()
+    while n < cs.b:
+        oracle.attend_explicit(v(cs.q[n:n + 1]), v(cs.C[n:n + 1]), Wk, Wv, cs.heads, cs.d,
+                               cs.softmax_scale)
+        n += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = time.perf_counter() - t0
+    log(f"[bench] cpu oracle: {n} sequences in {dt:.1f}s on {threads} threads")
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {cs.b} sequences of the same step, all {cs.heads} heads, explicit "
+                      f"K/V in float64 ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

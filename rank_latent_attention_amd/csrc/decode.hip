@@ -110,6 +110,63 @@ __global__ __launch_bounds__(256) void absorb_kernel(const QT *__restrict__ q,
   }
 }
 
+// MFMA form for bf16 queries (d % 32 == 0): per head, Q~_h[b][j] = q_h[b][:] . W^u_k[j][h d:(h+1) d]
+// is a [16 sequences x d] x [d x 16 rows] product per v_mfma_f32_16x16x32_bf16
+// chain.  Workgroup = (64 rows j, head h, 16 sequences); wavefront = 16 rows.
+// int8 W^u_k codes convert exactly to bf16; their column scales multiply q.
+template <typename WT>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__restrict__ q,
+                                                          const WT *__restrict__ Wk,
+                                                          const float *__restrict__ wscale,
+                                                          uint16_t *__restrict__ qt, int b, int r,
+                                                          int heads, int d, float scale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y, b0 = blockIdx.z * 16;
+  const int j0 = blockIdx.x * 64 + wave * 16;
+  const int64_t E = static_cast<int64_t>(heads) * d;
+  const int bb = b0 + (lane & 15);
+  const int j = j0 + (lane & 15);
+  const int kq = (lane >> 4) * 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < d; k0 += 32) {
+    const int i = k0 + kq;
+    u32x4 av = {0u, 0u, 0u, 0u}, bv = {0u, 0u, 0u, 0u};
+    if (bb < b) {
+      av = *reinterpret_cast<const u32x4 *>(q + (static_cast<int64_t>(bb) * heads + h) * d + i);
+      if (wscale) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(av[e] << 16) * wscale[h * d + i + 2 * e];
+          const float hi = __uint_as_float(av[e] & 0xFFFF0000u) * wscale[h * d + i + 2 * e + 1];
+          av[e] = pack_bf16x2(lo, hi);
+        }
+      }
+    }
+    if (j < r) {
+      if constexpr (sizeof(WT) == 2) {
+        bv = *reinterpret_cast<const u32x4 *>(Wk + static_cast<int64_t>(j) * E + h * d + i);
+      } else {
+        const u32x2 c = *reinterpret_cast<const u32x2 *>(Wk + static_cast<int64_t>(j) * E + h * d + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t word = c[e >> 1];
+          const int sh = 16 * (e & 1);
+          const int c0 = static_cast<int>(word << (24 - sh)) >> 24;
+          const int c1 = static_cast<int>(word << (16 - sh)) >> 24;
+          bv[e] = pack_bf16x2(static_cast<float>(c0), static_cast<float>(c1));
+        }
+      }
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                  __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int bo = b0 + 4 * (lane >> 4) + e;
+    if (bo < b && j < r) qt[(static_cast<int64_t>(bo) * heads + h) * r + j] = f32_to_bf16(acc[e] * scale);
+  }
+}
+
 // ------------------------------------------------------------------ float32 stream
 // One workgroup per (split, head, sequence); four wavefronts take every fourth
 // token of the split, each with its own online-softmax state, combined at the end.
@@ -265,8 +322,12 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   const int seq = pair / p.S;
   const int h0 = grp * p.group_heads;
   const int hg = min(p.group_heads, p.heads - h0);
-  const int64_t t_begin = static_cast<int64_t>(split) * p.chunk;
-  const int64_t t_end = min(p.L, t_begin + p.chunk);
+  // Split s owns token tiles s, s + S, s + 2S, ...: at any moment the
+  // workgroups of one sequence read neighbouring tiles, so the whole GPU
+  // streams a few contiguous regions instead of S far-apart ones.
+  const int64_t t_end = p.L;
+  const int64_t tiles_all = (p.L + T - 1) / T;
+  const int ntiles = split < tiles_all ? static_cast<int>((tiles_all - split + p.S - 1) / p.S) : 0;
   const int j0w = wave * rw;
 
   uint8_t *ct = smem + static_cast<size_t>(wave) * T * RS;
@@ -306,37 +367,32 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   }
   __syncthreads();
 
-  const int64_t span = t_end - t_begin;
-  const int ntiles = span > 0 ? static_cast<int>((span + T - 1) / T) : 0;
   const int units_per_row = rw / Tr::kElemsPerUnit;
   const int nunits = T * units_per_row;
 
   // ---- tile staging
   u32x4 buf[MAXU];
   float bscale[MAXU];
+  // Every lane loads unconditionally: rows past the end of the sequence re-read
+  // its last row (their scores are masked to -inf, so P is 0 for them) and
+  // units past the slice re-read its last unit (never stored).
   auto load_tile = [&](int64_t tile_t0) {
 #pragma unroll
     for (int k = 0; k < MAXU; ++k) {
-      const int u = lane + 64 * k;
-      buf[k] = u32x4{0u, 0u, 0u, 0u};
-      bscale[k] = 0.f;
-      if (u < nunits) {
-        const int row = u / units_per_row, col = u % units_per_row;
-        const int64_t t = tile_t0 + row;
-        if (t < t_end) {
-          const int64_t tok = static_cast<int64_t>(seq) * p.L + t;
-          const int j = j0w + col * Tr::kElemsPerUnit;
-          if constexpr (CT == CT_BF16) {
-            buf[k] = *reinterpret_cast<const u32x4 *>(p.C + (tok * r + j) * 2);
-          } else if constexpr (CT == CT_I4) {
-            const u32x2 v = *reinterpret_cast<const u32x2 *>(p.C + (tok * r + j) / 2);
-            buf[k] = u32x4{v.x, v.y, 0u, 0u};
-            bscale[k] = p.c_scales[tok * (r / 128) + j / 128];
-          } else {
-            buf[k] = *reinterpret_cast<const u32x4 *>(p.C + tok * r + j);
-            bscale[k] = p.c_scales[tok];
-          }
-        }
+      const int u = min(lane + 64 * k, nunits - 1);
+      const int row = u / units_per_row, col = u % units_per_row;
+      const int64_t t = min(tile_t0 + row, t_end - 1);
+      const int64_t tok = static_cast<int64_t>(seq) * p.L + t;
+      const int j = j0w + col * Tr::kElemsPerUnit;
+      if constexpr (CT == CT_BF16) {
+        buf[k] = *reinterpret_cast<const u32x4 *>(p.C + (tok * r + j) * 2);
+      } else if constexpr (CT == CT_I4) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(p.C + (tok * r + j) / 2);
+        buf[k] = u32x4{v.x, v.y, 0u, 0u};
+        bscale[k] = p.c_scales[tok * (r / 128) + j / 128];
+      } else {
+        buf[k] = *reinterpret_cast<const u32x4 *>(p.C + tok * r + j);
+        bscale[k] = p.c_scales[tok];
       }
     }
   };
@@ -373,11 +429,12 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
     }
   };
 
-  if (ntiles > 0) load_tile(t_begin);
+  const int64_t tile_stride = static_cast<int64_t>(p.S) * T;
+  if (ntiles > 0) load_tile(static_cast<int64_t>(split) * T);
   for (int it = 0; it < ntiles; ++it) {
-    const int64_t tile_t0 = t_begin + static_cast<int64_t>(it) * T;
+    const int64_t tile_t0 = (static_cast<int64_t>(split) + static_cast<int64_t>(it) * p.S) * T;
     store_tile();
-    if (it + 1 < ntiles) load_tile(tile_t0 + T);
+    if (it + 1 < ntiles) load_tile(tile_t0 + tile_stride);
     compiler_fence();
 
     // ---- partial scores over this wavefront's columns
@@ -534,9 +591,11 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 }
 
 // ------------------------------------------------------------------ merge
-// Workgroup (chunk jc of 128 latent rows, head h): for each sequence, the
-// log-sum-exp weights of its splits, the merged O~ rows of the chunk, and the
-// chunk's share of O~ W^u_v,h (float32) -> opj[jc][b][h][d].
+// Workgroup (chunk jc of 128 latent rows, head h, 16 sequences):
+//   1. log-sum-exp weights of every split (one wavefront per sequence),
+//   2. merged O~ rows of the chunk (16 B partial loads),
+//   3. the chunk's share of O~ W^u_v,h in float32 -> opj[jc][b][h][d].
+// W^u_v is read once per (chunk, head): the whole grid reads it once.
 template <typename PT, typename WT>
 __global__ __launch_bounds__(256) void merge_kernel(const PT *__restrict__ opart,
                                                     const float *__restrict__ ml,
@@ -544,71 +603,118 @@ __global__ __launch_bounds__(256) void merge_kernel(const PT *__restrict__ opart
                                                     const float *__restrict__ wscale,
                                                     float *__restrict__ opj, int b, int r,
                                                     int heads, int d, int S) {
-  constexpr int BB = 8;  // sequences per pass
-  __shared__ float wts[BB][kMaxSplits];
-  __shared__ float mv[BB][kMergeRows];
-  const int jc = blockIdx.x, h = blockIdx.y;
-  const int E = heads * d;
+  constexpr int BB = 16;
+  extern __shared__ float msm[];
+  float *wts = msm;                  // [BB][S]
+  float *mv = msm + BB * S;          // [BB][kMergeRows]
+  const int jc = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * BB;
+  const int nbb = min(BB, b - b0);
+  const int64_t E = static_cast<int64_t>(heads) * d;
   const int j0 = jc * kMergeRows;
   const int rows = min(kMergeRows, r - j0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int b0 = 0; b0 < b; b0 += BB) {
-    const int nbb = min(BB, b - b0);
-    // log-sum-exp weights (one wavefront per sequence)
-    for (int bi = wave; bi < nbb; bi += 4) {
-      const int64_t base = (static_cast<int64_t>(b0 + bi) * S) * heads + h;
-      float mx = -INFINITY;
-      for (int s = lane; s < S; s += 64) mx = fmaxf(mx, ml[2 * (base + static_cast<int64_t>(s) * heads)]);
-      mx = group_max<64>(mx);
-      float den = 0.f;
-      for (int s = lane; s < S; s += 64) {
-        const int64_t o = base + static_cast<int64_t>(s) * heads;
-        const float w = (mx == -INFINITY) ? 0.f : exp2f(ml[2 * o] - mx) * ml[2 * o + 1];
-        wts[bi][s] = w;
-        den += w;
-      }
-      den = group_sum<64>(den);
-      const float inv = den > 0.f ? 1.f / den : 0.f;
-      for (int s = lane; s < S; s += 64) wts[bi][s] *= inv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int bi = wave; bi < nbb; bi += 4) {
+    const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
+    float mx = -INFINITY;
+    for (int s = lane; s < S; s += 64) mx = fmaxf(mx, ml[2 * (base + static_cast<int64_t>(s) * heads)]);
+    mx = group_max<64>(mx);
+    float den = 0.f;
+    for (int s = lane; s < S; s += 64) {
+      const int64_t o = base + static_cast<int64_t>(s) * heads;
+      const float w = (mx == -INFINITY) ? 0.f : exp2f(ml[2 * o] - mx) * ml[2 * o + 1];
+      wts[bi * S + s] = w;
+      den += w;
     }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nbb * kMergeRows; idx += blockDim.x) {
-      const int bi = idx / kMergeRows, jj = idx % kMergeRows;
-      float acc = 0.f;
-      if (jj < rows) {
-        const int64_t base = (static_cast<int64_t>(b0 + bi) * S) * heads + h;
-        for (int s = 0; s < S; ++s) {
-          const float w = wts[bi][s];
-          if (w != 0.f) {
-            const int64_t o = (base + static_cast<int64_t>(s) * heads) * r + j0 + jj;
-            float v;
-            if constexpr (sizeof(PT) == 2)
-              v = bf16_to_f32(opart[o]);
-            else
-              v = opart[o];
-            acc = fmaf(w, v, acc);
+    den = group_sum<64>(den);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int s = lane; s < S; s += 64) wts[bi * S + s] *= inv;
+  }
+  __syncthreads();
+
+  if constexpr (sizeof(PT) == 2) {
+    // r % 32 == 0 on this path: 8 consecutive rows per thread, 16-byte loads
+    const int bi = tid >> 4, jj0 = (tid & 15) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (bi < nbb && jj0 < rows) {
+      const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
+      for (int s = 0; s < S; ++s) {
+        const float w = wts[bi * S + s];
+        if (w != 0.f) {
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(
+              opart + (base + static_cast<int64_t>(s) * heads) * r + j0 + jj0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xFFFF0000u), acc[2 * e + 1]);
           }
         }
       }
-      mv[bi][jj] = acc;
     }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nbb * d; idx += blockDim.x) {
-      const int i = idx % d, bi = idx / d;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mv[bi * kMergeRows + jj0 + e] = acc[e];
+  } else {
+    for (int idx = tid; idx < BB * kMergeRows; idx += blockDim.x) {
+      const int bi = idx / kMergeRows, jj = idx % kMergeRows;
       float acc = 0.f;
-      for (int jj = 0; jj < rows; ++jj) {
-        const int64_t wo = static_cast<int64_t>(j0 + jj) * E + h * d + i;
-        float w;
-        if constexpr (sizeof(WT) == 2)
-          w = bf16_to_f32(Wv[wo]);
-        else
-          w = static_cast<float>(Wv[wo]);
-        acc = fmaf(mv[bi][jj], w, acc);
+      if (bi < nbb && jj < rows) {
+        const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
+        for (int s = 0; s < S; ++s) {
+          const float w = wts[bi * S + s];
+          if (w != 0.f) acc = fmaf(w, opart[(base + static_cast<int64_t>(s) * heads) * r + j0 + jj], acc);
+        }
       }
-      if (wscale) acc = acc * wscale[h * d + i];
-      opj[((static_cast<int64_t>(jc) * b + b0 + bi) * heads + h) * d + i] = acc;
+      mv[idx] = acc;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+
+  // thread -> column i of the head, sequences g, g + groups, ...
+  const int groups = max(1, 256 / d);
+  const int i = tid % d, g = tid / d;
+  if (g < groups && i < d) {
+    float acc[BB];
+#pragma unroll
+    for (int k = 0; k < BB; ++k) acc[k] = 0.f;
+    const WT *wcol = Wv + static_cast<int64_t>(j0) * E + h * d + i;
+    int jj = 0;
+    for (; jj + 4 <= rows; jj += 4) {
+      float w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (sizeof(WT) == 2)
+          w[u] = bf16_to_f32(wcol[(jj + u) * E]);
+        else
+          w[u] = static_cast<float>(wcol[(jj + u) * E]);
+      }
+#pragma unroll
+      for (int k = 0; k < BB; ++k) {
+        const int bi = g + k * groups;
+        if (bi < nbb) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[k] = fmaf(mv[bi * kMergeRows + jj + u], w[u], acc[k]);
+        }
+      }
+    }
+    for (; jj < rows; ++jj) {
+      float w;
+      if constexpr (sizeof(WT) == 2)
+        w = bf16_to_f32(wcol[jj * E]);
+      else
+        w = static_cast<float>(wcol[jj * E]);
+#pragma unroll
+      for (int k = 0; k < BB; ++k) {
+        const int bi = g + k * groups;
+        if (bi < nbb) acc[k] = fmaf(mv[bi * kMergeRows + jj], w, acc[k]);
+      }
+    }
+    const float sc = wscale ? wscale[h * d + i] : 1.f;
+#pragma unroll
+    for (int k = 0; k < BB; ++k) {
+      const int bi = g + k * groups;
+      if (bi < nbb)
+        opj[((static_cast<int64_t>(jc) * b + b0 + bi) * heads + h) * d + i] = acc[k] * sc;
+    }
   }
 }
 
@@ -728,9 +834,24 @@ template <typename PT, typename WT>
 hipError_t launch_merge_t(const DecodeArgs &a, const DecodePlan &p, const PT *opart,
                           const float *ml, float *opj, hipStream_t s) {
   const int JC = (a.r + kMergeRows - 1) / kMergeRows;
-  merge_kernel<PT, WT><<<dim3(JC, a.heads), dim3(256), 0, s>>>(
+  const size_t lds = (static_cast<size_t>(16) * p.splits + 16 * kMergeRows) * sizeof(float);
+  auto kern = merge_kernel<PT, WT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
       opart, ml, static_cast<const WT *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
       p.splits);
+  return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t launch_absorb_mfma(const DecodeArgs &a, uint16_t *qt, hipStream_t s) {
+  const dim3 grid((a.r + 63) / 64, a.heads, (a.b + 15) / 16);
+  absorb_mfma_kernel<WT><<<grid, dim3(256), 0, s>>>(
+      static_cast<const uint16_t *>(a.q), static_cast<const WT *>(a.Wu_k), a.wu_scale_k, qt, a.b,
+      a.r, a.heads, a.d, a.softmax_scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -752,21 +873,33 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
     p.head_groups = heads;
     p.group_heads = 1;
   }
-  const int64_t max_splits = std::min<int64_t>(kMaxSplits, (L + 0) > 0 ? L : 1);
   int64_t S;
-  if (splits > 0) {
-    S = std::min<int64_t>(splits, max_splits);
-    p.chunk = (L + S - 1) / S;
+  if (p.mfma) {
+    // token tiles are dealt round-robin to the splits; no split is left empty
+    const int64_t tiles_all = (L + tile - 1) / tile;
+    if (splits > 0) {
+      S = splits;
+    } else {
+      const int64_t per = static_cast<int64_t>(b) * p.head_groups;
+      S = std::max<int64_t>(1, kNumCU / std::max<int64_t>(per, 1));
+    }
+    S = std::min<int64_t>(std::min<int64_t>(S, tiles_all), kMaxSplits);
+    p.chunk = 0;
+    p.splits = static_cast<int>(S);
   } else {
-    const int64_t per = static_cast<int64_t>(b) * p.head_groups;
-    S = std::max<int64_t>(1, kNumCU / std::max<int64_t>(per, 1));
-    if (!p.mfma) S = std::max<int64_t>(1, std::min<int64_t>(S, (L + 63) / 64));
-    S = std::min<int64_t>(S, std::max<int64_t>(1, (L + tile - 1) / tile));
-    S = std::min<int64_t>(S, max_splits);
-    p.chunk = (L + S - 1) / S;
-    p.chunk = (p.chunk + tile - 1) / tile * tile;
+    const int64_t max_splits = std::min<int64_t>(kMaxSplits, L);
+    if (splits > 0) {
+      S = std::min<int64_t>(splits, max_splits);
+      p.chunk = (L + S - 1) / S;
+    } else {
+      const int64_t per = static_cast<int64_t>(b) * p.head_groups;
+      S = std::max<int64_t>(1, kNumCU / std::max<int64_t>(per, 1));
+      S = std::max<int64_t>(1, std::min<int64_t>(S, (L + 63) / 64));
+      S = std::min<int64_t>(S, max_splits);
+      p.chunk = (L + S - 1) / S;
+    }
+    p.splits = static_cast<int>((L + p.chunk - 1) / p.chunk);
   }
-  p.splits = static_cast<int>((L + p.chunk - 1) / p.chunk);
   const size_t esz = p.mfma ? 2 : 4;
   p.qt_bytes = align256(static_cast<size_t>(b) * heads * r * esz);
   const size_t opart = align256(static_cast<size_t>(b) * p.splits * heads * r * esz);
@@ -794,6 +927,11 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
     LaunchTimer t("decode_absorb", s);
     if (!p.mfma) {
       e = launch_absorb_t<float, float, float>(a, static_cast<float *>(qt), s);
+    } else if (a.d % 32 == 0) {
+      if (a.wu_dtype == QSVD_I8)
+        e = launch_absorb_mfma<int8_t>(a, static_cast<uint16_t *>(qt), s);
+      else
+        e = launch_absorb_mfma<uint16_t>(a, static_cast<uint16_t *>(qt), s);
     } else if (a.wu_dtype == QSVD_I8) {
       e = launch_absorb_t<uint16_t, int8_t, uint16_t>(a, static_cast<uint16_t *>(qt), s);
     } else {

@@ -344,3 +344,16 @@ def c4_layer(l: int, r: int, E: int = 4096, p: float = 0.5, beta: float = 0.5, h
     """Stored int8 weights of prefill layer l (W^d' per column, [W^u_k | W^u_v] per column)."""
     return quantised_layer_inputs(E, r, p, beta, hadamard, (100400 + l,))
 
+
+
+def down_projection_int8(E: int, r: int, p: float, beta: float, hadamard: int, seed: tuple):
+    """Only W^d' = H1 U_r Sigma_r^beta as int8 per-column codes (the projection's weight)."""
+    U = haar_columns(E, r, rng(*seed, _U))
+    Wd = U * spectrum(p, E)[:r] ** beta
+    return int8_columns(_apply_block_hadamard_left(hadamard, Wd))
+
+
+def prefill_activations(M: int, E: int, frac: float = 0.01, gain: float = 50.0, seed: int = 1004):
+    """Prefill input rows X [M][E] (float64) with the outlier channels of the 7B shape."""
+    ch = outlier_channels(E, frac, rng(seed, _OUTLIER))
+    return activations(M, E, ch, gain, rng(seed, _X, 0))

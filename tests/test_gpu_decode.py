@@ -69,9 +69,9 @@ BF16_SHAPES = [
     # E, heads, d, r, b, L
     (256, 4, 64, 128, 2, 1),
     (256, 4, 64, 256, 3, 17),
-    (512, 4, 128, 768, 2, 300),
+    (1024, 8, 128, 768, 2, 300),
     (1024, 16, 64, 512, 2, 1000),
-    (2048, 16, 128, 2304, 1, 77),
+    (2560, 20, 128, 2304, 1, 77),
     (4096, 32, 128, 1536, 2, 700),
     (5120, 40, 128, 2304, 1, 333),
     (768, 6, 128, 96, 2, 65),
