@@ -189,14 +189,9 @@ static qsvd_status_t validate_decode_shape(int32_t b, int64_t L, int32_t r, int3
       return fail(QSVD_ERR_INVALID, "decode: r = %d must be a positive multiple of 32", r);
     if (c_dtype == QSVD_I4 && r % 128 != 0)
       return fail(QSVD_ERR_INVALID, "decode: int4 cache needs r %% 128 == 0 (r = %d)", r);
-    int W = 1;
-    for (int w : {8, 4, 2, 1})
-      if (r % (32 * w) == 0) {
-        W = w;
-        break;
-      }
-    if (r / W / 16 > 18)
-      return fail(QSVD_ERR_UNSUPPORTED, "decode: r = %d exceeds the per-wavefront column budget", r);
+    if (!qsvd::mfma_shape(r, heads, c_dtype, nullptr))
+      return fail(QSVD_ERR_UNSUPPORTED,
+                  "decode: r = %d has no stream-kernel shape (r = W * 32 * k, W <= 8, k <= 12)", r);
   } else {
     return fail(QSVD_ERR_INVALID, "decode: c_dtype %s", dtype_name(c_dtype));
   }

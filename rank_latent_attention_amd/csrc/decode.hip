@@ -12,26 +12,32 @@
 //   decode_stream   per (sequence, L-split, head group): for each token tile
 //                   S = C_tile q~^T (scores of all heads), online softmax,
 //                   O~ <- O~ * alpha + P^T C_tile; writes (m, l, O~ / l)
-//   decode_merge    per (head, 128-row chunk of r): log-sum-exp merge of the
-//                   splits and the chunk's share of O~ W^u_v,h
+//   decode_merge    per (head, 128-row chunk of r, 16 sequences): log-sum-exp
+//                   merge of the splits and the chunk's share of O~ W^u_v,h
 //   decode_finalize sum of the chunk shares -> O
 //
 // The WSVD digest ("Method, 3.4") folds the value up-projection into the
 // output side in the same way; K and V never exist in memory.
 //
-// MFMA stream kernel layout (bf16 / int4 / int8 caches).  A workgroup has W
-// wavefronts; wavefront w owns latent columns [w*rw, (w+1)*rw) of every token
-// (rw = r / W).  Per tile of T tokens:
-//   1. the wavefront moves its C slice (T x rw) from HBM through registers
-//      (128-bit loads, next tile prefetched) into a wavefront-private LDS
-//      region, dequantising int4/int8 codes to bf16 on the way;
-//   2. partial scores over its columns: v_mfma_f32_16x16x32_bf16 with the
-//      C rows as A and the absorbed queries (kept in registers) as B;
-//   3. partial scores are summed across wavefronts through LDS; the owners of
-//      each head do the online-softmax bookkeeping and write P (bf16);
-//   4. O~ (heads x rw, float32, in registers) is rescaled and accumulates
-//      P^T C_tile with C read transposed from LDS (16x16x32 for T = 32,
-//      16x16x16 for T = 16).
+// MFMA stream kernel (bf16 / int8 / int4 caches).  A workgroup has W
+// wavefronts; wavefront w owns RW = 32 * NKB latent columns of every token.
+// Per tile of 32 tokens:
+//   1. the tile's C slice arrives in registers (16-byte loads issued one tile
+//      ahead) laid out as the A operand of v_mfma_f32_16x16x32_bf16: lane l
+//      holds 8 columns of token l % 16.  Codes of quantised caches are
+//      dequantised to bf16 here;
+//   2. partial scores over the wavefront's columns: A = C rows, B = absorbed
+//      queries (kept in registers for the whole split);
+//   3. the same registers go to a wavefront-private LDS tile (row-major), and
+//      the loads of the next tile are issued;
+//   4. partial scores are summed across wavefronts through LDS; one pass over
+//      (head, token pair) does the online-softmax bookkeeping and writes P as
+//      the A operand of the value product;
+//   5. O~ (heads x RW, float32 accumulators) is rescaled and accumulates
+//      P^T C_tile, the C operand read token-major out of LDS with the gfx950
+//      transposing load ds_read_b64_tr_b16.
+// Two workgroup barriers per tile; the loads of tile i+1 are in flight during
+// steps 4-5 of tile i and step 1 of tile i+1 waits for them.
 #include "device_common.h"
 #include "qsvd_internal.h"
 
@@ -256,56 +262,78 @@ struct StreamParams {
   int r;
   int heads;
   int S;
-  int64_t chunk;
   int G;            // head groups
-  int group_heads;  // heads per group (last may be smaller)
-  int nb;           // 16-column blocks per wavefront
+  int group_heads;  // heads per group (the last group may have fewer)
   int ntasks;
 };
 
+// Cache element formats.  A 16-byte load carries EPL elements; they feed KPL
+// consecutive 32-wide K blocks of the score product.
 template <int CT>
 struct CacheTraits;
 template <>
 struct CacheTraits<CT_BF16> {
-  static constexpr int kElemsPerUnit = 8;  // 16 bytes
-  static constexpr int kUnitBytes = 16;
-};
-template <>
-struct CacheTraits<CT_I4> {
-  static constexpr int kElemsPerUnit = 16;  // 8 bytes
-  static constexpr int kUnitBytes = 8;
+  static constexpr int EPL = 8;
+  __device__ static int64_t byte_offset(int64_t elem) { return elem * 2; }
 };
 template <>
 struct CacheTraits<CT_I8> {
-  static constexpr int kElemsPerUnit = 16;  // 16 bytes
-  static constexpr int kUnitBytes = 16;
+  static constexpr int EPL = 16;
+  __device__ static int64_t byte_offset(int64_t elem) { return elem; }
+};
+template <>
+struct CacheTraits<CT_I4> {
+  static constexpr int EPL = 32;
+  __device__ static int64_t byte_offset(int64_t elem) { return elem / 2; }
 };
 
-__host__ __device__ constexpr int lds_row_stride(int rw) { return rw * 2 + 16; }
+__host__ __device__ constexpr int ct_row_stride(int nkb) { return nkb * 64 + 16; }
 
-__host__ __device__ constexpr size_t stream_lds_bytes(int W, int T, int rw, int HGP) {
-  return static_cast<size_t>(W) * T * lds_row_stride(rw) +            // C tiles
-         static_cast<size_t>(W) * (T / 16) * (HGP / 16) * 64 * 16 +  // partial scores
-         static_cast<size_t>(HGP / 16) * 64 * (T / 4) * 2 +          // P
-         static_cast<size_t>(HGP) * 4 * 3;                           // alpha, m, l
+// LDS bytes of the stream kernel: wavefront C tiles | partial scores | P | alpha, m, l.
+__host__ __device__ constexpr size_t stream_lds_bytes(int W, int NHB, int NKB, int T) {
+  return static_cast<size_t>(W) * T * ct_row_stride(NKB) +
+         static_cast<size_t>(W) * (T / 16) * NHB * 64 * 16 + static_cast<size_t>(NHB) * 64 * T / 2 +
+         static_cast<size_t>(NHB) * 16 * 4 * 3;
 }
 
-template <int CT, int HGP, int MAXNB, int T>
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t *p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16 *)(
+          reinterpret_cast<__attribute__((address_space(3))) uint8_t *>(
+              reinterpret_cast<uintptr_t>(p))));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// bf16 pair of two dequantised codes c * s (float32 product, round to nearest even).
+__device__ __forceinline__ uint32_t dq_pair(int c0, int c1, float s) {
+  return pack_bf16x2(static_cast<float>(c0) * s, static_cast<float>(c1) * s);
+}
+
+// Template parameters: cache format CT, NHB 16-head blocks per workgroup, NKB
+// 32-column K blocks per wavefront (RW = 32 NKB columns), T tokens per tile
+// (32, or 16 when a 32-token tile does not fit in LDS).  The wavefront count
+// W = blockDim.x / 64 satisfies r = W * RW.
+template <int CT, int NHB, int NKB, int T>
 __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   using Tr = CacheTraits<CT>;
-  constexpr int NHB = HGP / 16;
-  constexpr int NTB = T / 16;
-  constexpr int KPL = T / 4;          // tokens per lane in the O~ MFMA operand
-  constexpr int MAXKB = MAXNB / 2;    // 32-column score K-blocks
-  constexpr int MAXU = (T * MAXNB * 16 / Tr::kElemsPerUnit + 63) / 64;  // load units per lane
+  constexpr int EPL = Tr::EPL;
+  constexpr int KPL = EPL / 8;          // K blocks per 16-byte load
+  constexpr int NLD = NKB / KPL;        // loads per 16-token row block
+  constexpr int NTB = T / 16;           // 16-token row blocks per tile
+  constexpr int NJB = NKB * 2;          // 16-column blocks of O~
+  constexpr int RW = NKB * 32;          // columns per wavefront
+  constexpr int RS = ct_row_stride(NKB);
+  constexpr int PPL = T / 4;            // P elements per lane (value-product A operand)
+  static_assert(NKB % KPL == 0, "wavefront columns must be whole 16-byte loads");
+  static_assert(T == 16 || T == 32, "tile");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int W = blockDim.x >> 6;
   const int nthreads = blockDim.x;
-  const int nb = p.nb, rw = nb * 16, nkb = nb / 2;
-  const int RS = lds_row_stride(rw);
   const int r = p.r;
+  const int li = lane & 15, lg = lane >> 4;
 
   // XCD-aware task order: workgroup i runs on XCD i % 8; give each XCD a
   // contiguous run of tasks so the head groups of one (sequence, split) share
@@ -322,163 +350,152 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   const int seq = pair / p.S;
   const int h0 = grp * p.group_heads;
   const int hg = min(p.group_heads, p.heads - h0);
-  // Split s owns token tiles s, s + S, s + 2S, ...: at any moment the
-  // workgroups of one sequence read neighbouring tiles, so the whole GPU
-  // streams a few contiguous regions instead of S far-apart ones.
-  const int64_t t_end = p.L;
-  const int64_t tiles_all = (p.L + T - 1) / T;
+  // Split s owns token tiles s, s + S, s + 2S, ...: the workgroups of one
+  // sequence read neighbouring tiles at any moment.
+  const int64_t L = p.L;
+  const int64_t tiles_all = (L + T - 1) / T;
   const int ntiles = split < tiles_all ? static_cast<int>((tiles_all - split + p.S - 1) / p.S) : 0;
-  const int j0w = wave * rw;
+  const int j0w = wave * RW;
 
   uint8_t *ct = smem + static_cast<size_t>(wave) * T * RS;
-  float *spart = reinterpret_cast<float *>(smem + static_cast<size_t>(W) * T * RS);
-  uint16_t *pl = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(spart) +
-                                              static_cast<size_t>(W) * NTB * NHB * 64 * 16);
-  float *alpha_s = reinterpret_cast<float *>(pl + NHB * 64 * KPL);
-  float *m_s = alpha_s + HGP;
-  float *l_s = m_s + HGP;
+  f32x4 *spart = reinterpret_cast<f32x4 *>(smem + static_cast<size_t>(W) * T * RS);
+  uint16_t *pl = reinterpret_cast<uint16_t *>(spart + static_cast<size_t>(W) * NTB * NHB * 64);
+  float *alpha_s = reinterpret_cast<float *>(pl + NHB * 64 * PPL);
+  float *m_s = alpha_s + NHB * 16;
+  float *l_s = m_s + NHB * 16;
 
-  // absorbed queries as the B operand of the score MFMA: lane holds
-  // q~[h = hb*16 + lane%16][j = kb*32 + (lane/16)*8 .. +8]
-  bf16x8 qf[NHB][MAXKB];
+  // Absorbed queries as the B operand of the score product.  K block
+  // kb = KPL * ld + s of lane group g covers columns
+  // j0w + 32 KPL ld + EPL g + 8 s + (0..7): the order in which the 16-byte
+  // cache loads deliver them.
+  bf16x8 qf[NHB][NKB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int kb = 0; kb < MAXKB; ++kb) {
-      const int h = hb * 16 + (lane & 15);
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int h = hb * 16 + li;
+      const int ld = kb / KPL, s = kb % KPL;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (kb < nkb && h < hg) {
-        const int j = j0w + kb * 32 + (lane >> 4) * 8;
-        v = *reinterpret_cast<const u32x4 *>(
-            p.qt + (static_cast<int64_t>(seq) * p.heads + h0 + h) * r + j);
+      if (h < hg) {
+        const int j = j0w + 32 * KPL * ld + EPL * lg + 8 * s;
+        v = *reinterpret_cast<const u32x4 *>(p.qt + (static_cast<int64_t>(seq) * p.heads + h0 + h) * r + j);
       }
       qf[hb][kb] = __builtin_bit_cast(bf16x8, v);
     }
 
-  f32x4 oacc[NHB][MAXNB];
+  f32x4 oacc[NHB][NJB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int jb = 0; jb < MAXNB; ++jb) oacc[hb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < NJB; ++jb) oacc[hb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int i = tid; i < HGP; i += nthreads) {
+  for (int i = tid; i < NHB * 16; i += nthreads) {
     m_s[i] = -INFINITY;
     l_s[i] = 0.f;
   }
+
+  // ---- tile loads: row block tb, load ld -> stage[tb][ld]
+  u32x4 stage[NTB][NLD];
+  float sscale[NTB][NLD];
+  const int64_t row_base = static_cast<int64_t>(seq) * L;
+  auto load_rows = [&](int64_t t0, int tb) {
+    // rows past the end of the sequence re-read its last row; their scores
+    // are masked to -inf below, so their P is 0
+    const int64_t tok = row_base + min(t0 + tb * 16 + li, L - 1);
+#pragma unroll
+    for (int ld = 0; ld < NLD; ++ld) {
+      const int64_t col = j0w + 32 * KPL * ld + EPL * lg;
+      stage[tb][ld] = *reinterpret_cast<const u32x4 *>(p.C + Tr::byte_offset(tok * r + col));
+      if constexpr (CT == CT_I8) sscale[tb][ld] = p.c_scales[tok];
+      if constexpr (CT == CT_I4) sscale[tb][ld] = p.c_scales[tok * (r / 128) + col / 128];
+    }
+  };
+
+  if (ntiles > 0) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) load_rows(static_cast<int64_t>(split) * T, tb);
+  }
   __syncthreads();
 
-  const int units_per_row = rw / Tr::kElemsPerUnit;
-  const int nunits = T * units_per_row;
-
-  // ---- tile staging
-  u32x4 buf[MAXU];
-  float bscale[MAXU];
-  // Every lane loads unconditionally: rows past the end of the sequence re-read
-  // its last row (their scores are masked to -inf, so P is 0 for them) and
-  // units past the slice re-read its last unit (never stored).
-  auto load_tile = [&](int64_t tile_t0) {
-#pragma unroll
-    for (int k = 0; k < MAXU; ++k) {
-      const int u = min(lane + 64 * k, nunits - 1);
-      const int row = u / units_per_row, col = u % units_per_row;
-      const int64_t t = min(tile_t0 + row, t_end - 1);
-      const int64_t tok = static_cast<int64_t>(seq) * p.L + t;
-      const int j = j0w + col * Tr::kElemsPerUnit;
-      if constexpr (CT == CT_BF16) {
-        buf[k] = *reinterpret_cast<const u32x4 *>(p.C + (tok * r + j) * 2);
-      } else if constexpr (CT == CT_I4) {
-        const u32x2 v = *reinterpret_cast<const u32x2 *>(p.C + (tok * r + j) / 2);
-        buf[k] = u32x4{v.x, v.y, 0u, 0u};
-        bscale[k] = p.c_scales[tok * (r / 128) + j / 128];
-      } else {
-        buf[k] = *reinterpret_cast<const u32x4 *>(p.C + tok * r + j);
-        bscale[k] = p.c_scales[tok];
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int k = 0; k < MAXU; ++k) {
-      const int u = lane + 64 * k;
-      if (u < nunits) {
-        const int row = u / units_per_row, col = u % units_per_row;
-        uint8_t *dst = ct + row * RS + col * Tr::kElemsPerUnit * 2;
-        if constexpr (CT == CT_BF16) {
-          *reinterpret_cast<u32x4 *>(dst) = buf[k];
-        } else {
-          uint32_t out[8];
-#pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            int c0, c1;
-            if constexpr (CT == CT_I4) {
-              const uint32_t word = buf[k][e >> 3];
-              c0 = static_cast<int>(word << (28 - 4 * (e & 7))) >> 28;
-              c1 = static_cast<int>(word << (24 - 4 * (e & 7))) >> 28;
-            } else {
-              const uint32_t word = buf[k][e >> 2];
-              c0 = static_cast<int>(word << (24 - 8 * (e & 3))) >> 24;
-              c1 = static_cast<int>(word << (16 - 8 * (e & 3))) >> 24;
-            }
-            out[e >> 1] = pack_bf16x2(static_cast<float>(c0) * bscale[k],
-                                      static_cast<float>(c1) * bscale[k]);
-          }
-          *reinterpret_cast<u32x4 *>(dst) = u32x4{out[0], out[1], out[2], out[3]};
-          *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{out[4], out[5], out[6], out[7]};
-        }
-      }
-    }
-  };
-
-  const int64_t tile_stride = static_cast<int64_t>(p.S) * T;
-  if (ntiles > 0) load_tile(static_cast<int64_t>(split) * T);
   for (int it = 0; it < ntiles; ++it) {
     const int64_t tile_t0 = (static_cast<int64_t>(split) + static_cast<int64_t>(it) * p.S) * T;
-    store_tile();
-    if (it + 1 < ntiles) load_tile(tile_t0 + tile_stride);
-    compiler_fence();
+    const bool more = it + 1 < ntiles;
+    const int64_t next_t0 = tile_t0 + static_cast<int64_t>(p.S) * T;
 
-    // ---- partial scores over this wavefront's columns
+    // ---- 1-3. per 16-token row block: bf16 A operands, partial scores over
+    // this wavefront's columns, the rows to LDS, then the next tile's loads
     f32x4 sacc[NTB][NHB];
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
+    for (int tb = 0; tb < NTB; ++tb) {
+      u32x4 cv[NKB];
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld) {
+        if constexpr (CT == CT_BF16) {
+          cv[ld] = stage[tb][ld];
+        } else if constexpr (CT == CT_I8) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            uint32_t o[4];
+#pragma unroll
+            for (int w2 = 0; w2 < 2; ++w2) {
+              const uint32_t word = stage[tb][ld][2 * s + w2];
+              o[2 * w2] = dq_pair(static_cast<int>(word << 24) >> 24,
+                                  static_cast<int>(word << 16) >> 24, sscale[tb][ld]);
+              o[2 * w2 + 1] = dq_pair(static_cast<int>(word << 8) >> 24,
+                                      static_cast<int>(word) >> 24, sscale[tb][ld]);
+            }
+            cv[2 * ld + s] = u32x4{o[0], o[1], o[2], o[3]};
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t word = stage[tb][ld][s];
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[e] = dq_pair(static_cast<int>(word << (28 - 8 * e)) >> 28,
+                             static_cast<int>(word << (24 - 8 * e)) >> 28, sscale[tb][ld]);
+            cv[4 * ld + s] = u32x4{o[0], o[1], o[2], o[3]};
+          }
+        }
+      }
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) sacc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < MAXKB; ++kb) {
-      if (kb < nkb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          const u32x4 a = *reinterpret_cast<const u32x4 *>(
-              ct + (tb * 16 + (lane & 15)) * RS + kb * 64 + (lane >> 4) * 16);
+        for (int hb = 0; hb < NHB; ++hb)
+          sacc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, cv[kb]), qf[hb][kb], sacc[tb][hb], 0, 0, 0);
 #pragma unroll
-          for (int hb = 0; hb < NHB; ++hb)
-            sacc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a), qf[hb][kb], sacc[tb][hb], 0, 0, 0);
-        }
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int ld = kb / KPL, s = kb % KPL;
+        const int jl = 32 * KPL * ld + EPL * lg + 8 * s;
+        *reinterpret_cast<u32x4 *>(ct + (tb * 16 + li) * RS + jl * 2) = cv[kb];
       }
+      if (more) load_rows(next_t0, tb);
     }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
-        *reinterpret_cast<f32x4 *>(spart + (((wave * NTB + tb) * NHB + hb) * 64 + lane) * 4) =
-            sacc[tb][hb];
+      for (int hb = 0; hb < NHB; ++hb) spart[((wave * NTB + tb) * NHB + hb) * 64 + lane] = sacc[tb][hb];
     __syncthreads();
 
-    // ---- cross-wavefront sum + online softmax; T/2 lanes per head, 2 tokens each
-    for (int tau = tid; tau < HGP * (T / 2); tau += nthreads) {
-      const int h = tau / (T / 2), u = tau % (T / 2), t0 = 2 * u;
+    // ---- 4. cross-wavefront sum + online softmax; T/2 lanes per head, 2 tokens each
+    for (int item = tid; item < NHB * 16 * (T / 2); item += nthreads) {
+      const int h = item / (T / 2), u = item % (T / 2), t0 = 2 * u;
       const int tb = t0 >> 4, hb = h >> 4;
       const int ln = 16 * ((t0 & 15) >> 2) + (h & 15);
-      const int i0 = t0 & 3;
+      const int e0 = t0 & 3;
       float s0 = 0.f, s1 = 0.f;
       for (int w = 0; w < W; ++w) {
-        const float *src = spart + (((w * NTB + tb) * NHB + hb) * 64 + ln) * 4 + i0;
-        s0 += src[0];
-        s1 += src[1];
+        const float *src = reinterpret_cast<const float *>(spart + ((w * NTB + tb) * NHB + hb) * 64 + ln);
+        const float2 v = *reinterpret_cast<const float2 *>(src + e0);
+        s0 += v.x;
+        s1 += v.y;
       }
-      if (tile_t0 + t0 >= t_end) s0 = -INFINITY;
-      if (tile_t0 + t0 + 1 >= t_end) s1 = -INFINITY;
+      if (tile_t0 + t0 >= L) s0 = -INFINITY;
+      if (tile_t0 + t0 + 1 >= L) s1 = -INFINITY;
       const float mx = group_max<T / 2>(fmaxf(s0, s1));
       const float m_old = m_s[h];
       const float m_new = fmaxf(m_old, mx);
@@ -487,83 +504,56 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       const uint16_t p1 = f32_to_bf16(exp2f(s1 - m_new));
       const float psum = group_sum<T / 2>(bf16_to_f32(p0) + bf16_to_f32(p1));
       if (u == 0) {
-        const float l_old = l_s[h];
         m_s[h] = m_new;
-        l_s[h] = fmaf(l_old, alpha, psum);
+        l_s[h] = fmaf(l_s[h], alpha, psum);
         alpha_s[h] = alpha;
       }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int t = t0 + e;
-        const int g = (t & 15) >> 2, kk = (t >> 4) * 4 + (t & 3);
-        pl[(hb * 64 + g * 16 + (h & 15)) * KPL + kk] = e ? p1 : p0;
-      }
+      // P as the A operand of the value product: lane 16 (t / PPL) + h % 16, element t % PPL
+      uint16_t *pdst = pl + (hb * 64 + 16 * (t0 / PPL) + (h & 15)) * PPL + (t0 % PPL);
+      *reinterpret_cast<uint32_t *>(pdst) = static_cast<uint32_t>(p0) | (static_cast<uint32_t>(p1) << 16);
     }
     __syncthreads();
 
-    // ---- O~ = O~ * alpha + P^T C_tile
+    // ---- 5. O~ = O~ * alpha + P^T C_tile
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      float al[4];
+      const f32x4 al = *reinterpret_cast<const f32x4 *>(alpha_s + hb * 16 + 4 * lg);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = alpha_s[hb * 16 + 4 * (lane >> 4) + i];
+      for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-      for (int jb = 0; jb < MAXNB; ++jb)
-        if (jb < nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[hb][jb][i] *= al[i];
+        for (int e = 0; e < 4; ++e) oacc[hb][jb][e] *= al[e];
     }
+    // B operand: tokens PPL g + (0..PPL-1) of column 16 jb + lane % 16, by
+    // transposing 8-byte reads of 4 tokens each (lane i of a 16-lane group
+    // supplies row i / 4 and columns 4 (i % 4) .. +3 of a 4 x 16 block).
+    const uint8_t *trb = ct + (PPL * lg + (li >> 2)) * RS + (4 * (li & 3)) * 2;
     if constexpr (T == 32) {
       bf16x8 pa[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        pa[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                                pl + (hb * 64 + lane) * KPL));
+        pa[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(pl + (hb * 64 + lane) * PPL));
 #pragma unroll
-      for (int jb = 0; jb < MAXNB; ++jb) {
-        if (jb < nb) {
-          const uint16_t *col = reinterpret_cast<const uint16_t *>(ct) + jb * 16 + (lane & 15);
-          const int rs2 = RS / 2;
-          const int g4 = 4 * (lane >> 4);
-          uint32_t w[4];
+      for (int jb = 0; jb < NJB; ++jb) {
+        const bf16x4 lo = lds_read_tr16(trb + jb * 32);
+        const bf16x4 hi = lds_read_tr16(trb + 4 * RS + jb * 32);
+        const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int kk = 0; kk < 8; kk += 2) {
-            const int ta = (kk >> 2) * 16 + g4 + (kk & 3);
-            w[kk >> 1] = static_cast<uint32_t>(col[ta * rs2]) |
-                         (static_cast<uint32_t>(col[(ta + 1) * rs2]) << 16);
-          }
-          const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb)
-            oacc[hb][jb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[hb], bv, oacc[hb][jb], 0, 0, 0);
-        }
+        for (int hb = 0; hb < NHB; ++hb)
+          oacc[hb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[hb], bv, oacc[hb][jb], 0, 0, 0);
       }
     } else {
       bf16x4 pa[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        pa[hb] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(
-                                                pl + (hb * 64 + lane) * KPL));
+        pa[hb] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(pl + (hb * 64 + lane) * PPL));
 #pragma unroll
-      for (int jb = 0; jb < MAXNB; ++jb) {
-        if (jb < nb) {
-          const uint16_t *col = reinterpret_cast<const uint16_t *>(ct) + jb * 16 + (lane & 15);
-          const int rs2 = RS / 2;
-          const int g4 = 4 * (lane >> 4);
-          const uint32_t w0 = static_cast<uint32_t>(col[g4 * rs2]) |
-                              (static_cast<uint32_t>(col[(g4 + 1) * rs2]) << 16);
-          const uint32_t w1 = static_cast<uint32_t>(col[(g4 + 2) * rs2]) |
-                              (static_cast<uint32_t>(col[(g4 + 3) * rs2]) << 16);
-          const bf16x4 bv = __builtin_bit_cast(bf16x4, u32x2{w0, w1});
+      for (int jb = 0; jb < NJB; ++jb) {
+        const bf16x4 bv = lds_read_tr16(trb + jb * 32);
 #pragma unroll
-          for (int hb = 0; hb < NHB; ++hb)
-            oacc[hb][jb] =
-                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[hb], bv, oacc[hb][jb], 0, 0, 0);
-        }
+        for (int hb = 0; hb < NHB; ++hb)
+          oacc[hb][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[hb], bv, oacc[hb][jb], 0, 0, 0);
       }
     }
-    compiler_fence();
   }
   __syncthreads();
 
@@ -572,16 +562,14 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = hb * 16 + 4 * (lane >> 4) + i;
+    for (int e = 0; e < 4; ++e) {
+      const int h = hb * 16 + 4 * lg + e;
       if (h < hg) {
         const float l = l_s[h];
         const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *dst = p.opart + (pbase + h) * r + j0w + li;
 #pragma unroll
-        for (int jb = 0; jb < MAXNB; ++jb)
-          if (jb < nb)
-            p.opart[(pbase + h) * r + j0w + jb * 16 + (lane & 15)] =
-                f32_to_bf16(oacc[hb][jb][i] * inv);
+        for (int jb = 0; jb < NJB; ++jb) dst[jb * 16] = f32_to_bf16(oacc[hb][jb][e] * inv);
       }
     }
   for (int h = tid; h < hg; h += nthreads) {
@@ -590,6 +578,129 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA merge
+// Workgroup (chunk jc of kMergeRows latent rows, head h, 16 sequences):
+//   1. log-sum-exp weights of every split (one wavefront per sequence);
+//   2. merged O~ rows of the chunk (8 rows per thread, 16-byte partial
+//      loads), written to LDS as the A operand of v_mfma_f32_16x16x32_bf16
+//      (M = 16 sequences, K = latent rows);
+//   3. the chunk of W^u_v,h (kMergeRows x d) to LDS as bf16 (int8 codes are
+//      exact in bf16; their column scales multiply the result);
+//   4. O~ W^u_v,h with the B operand read by transposing LDS loads ->
+//      opj[jc][b][h][:] (float32).
+// W^u_v is read once per (chunk, head, 16 sequences).
+template <typename WT>
+__global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restrict__ opart,
+                                                         const float *__restrict__ ml,
+                                                         const WT *__restrict__ Wv,
+                                                         const float *__restrict__ wscale,
+                                                         float *__restrict__ opj, int b, int r,
+                                                         int heads, int d, int S) {
+  constexpr int BB = 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t msm[];
+  const int WRS = d * 2 + 16;                                       // W chunk row stride (bytes)
+  uint8_t *wl = msm;                                                // [kMergeRows][WRS]
+  u32x4 *aop = reinterpret_cast<u32x4 *>(msm + kMergeRows * WRS);   // [kMergeRows/32][64]
+  float *wts = reinterpret_cast<float *>(aop + (kMergeRows / 32) * 64);  // [BB][S]
+  const int jc = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * BB;
+  const int nbb = min(BB, b - b0);
+  const int64_t E = static_cast<int64_t>(heads) * d;
+  const int j0 = jc * kMergeRows;
+  const int rows = min(kMergeRows, r - j0);  // multiple of 32
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // 1. split weights
+  for (int bi = wave; bi < nbb; bi += 4) {
+    const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
+    float mx = -INFINITY;
+    for (int s = lane; s < S; s += 64) mx = fmaxf(mx, ml[2 * (base + static_cast<int64_t>(s) * heads)]);
+    mx = group_max<64>(mx);
+    float den = 0.f;
+    for (int s = lane; s < S; s += 64) {
+      const int64_t o = base + static_cast<int64_t>(s) * heads;
+      const float w = (mx == -INFINITY) ? 0.f : exp2f(ml[2 * o] - mx) * ml[2 * o + 1];
+      wts[bi * S + s] = w;
+      den += w;
+    }
+    den = group_sum<64>(den);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int s = lane; s < S; s += 64) wts[bi * S + s] *= inv;
+  }
+
+  // 3. W^u_v chunk -> LDS (bf16), 16 output bytes per thread per pass
+  {
+    const int units = d / 8;  // 16-byte bf16 units per row
+    for (int u = tid; u < rows * units; u += 256) {
+      const int row = u / units, c8 = (u % units) * 8;
+      const WT *src = Wv + static_cast<int64_t>(j0 + row) * E + static_cast<int64_t>(h) * d + c8;
+      u32x4 v;
+      if constexpr (sizeof(WT) == 2) {
+        v = *reinterpret_cast<const u32x4 *>(src);
+      } else {
+        const u32x2 c = *reinterpret_cast<const u32x2 *>(src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t word = c[e >> 1];
+          const int sh = 16 * (e & 1);
+          v[e] = pack_bf16x2(static_cast<float>(static_cast<int>(word << (24 - sh)) >> 24),
+                             static_cast<float>(static_cast<int>(word << (16 - sh)) >> 24));
+        }
+      }
+      *reinterpret_cast<u32x4 *>(wl + row * WRS + c8 * 2) = v;
+    }
+  }
+  __syncthreads();
+
+  // 2. merged O~ rows: thread (sequence tid / 16, rows 8 (tid % 16) .. +8)
+  {
+    const int bi = tid >> 4, jj0 = (tid & 15) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (bi < nbb && jj0 < rows) {
+      const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
+      for (int s = 0; s < S; ++s) {
+        const float w = wts[bi * S + s];
+        if (w != 0.f) {
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(
+              opart + (base + static_cast<int64_t>(s) * heads) * r + j0 + jj0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xFFFF0000u), acc[2 * e + 1]);
+          }
+        }
+      }
+    }
+    // A operand of K block jj0 / 32: lane 16 ((jj0 / 8) % 4) + sequence
+    aop[(jj0 >> 5) * 64 + 16 * ((jj0 >> 3) & 3) + bi] =
+        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  }
+  __syncthreads();
+
+  // 4. O~ W^u_v,h: wavefront w takes 16-column blocks w, w + 4, ...
+  const int li = lane & 15, lg = lane >> 4;
+  const int nkb = rows / 32;
+  for (int nb = wave; nb < d / 16; nb += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t *trb = wl + (8 * lg + (li >> 2)) * WRS + (nb * 16 + 4 * (li & 3)) * 2;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const bf16x4 lo = lds_read_tr16(trb + (32 * kb) * WRS);
+      const bf16x4 hi = lds_read_tr16(trb + (32 * kb + 4) * WRS);
+      const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aop[kb * 64 + lane]), bv,
+                                                    acc, 0, 0, 0);
+    }
+    const int col = nb * 16 + li;
+    const float sc = wscale ? wscale[static_cast<int64_t>(h) * d + col] : 1.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int bi = 4 * lg + e;
+      if (bi < nbb) opj[((static_cast<int64_t>(jc) * b + b0 + bi) * heads + h) * d + col] = acc[e] * sc;
+    }
+  }
+}
+
+
 // ------------------------------------------------------------------ merge
 // Workgroup (chunk jc of 128 latent rows, head h, 16 sequences):
 //   1. log-sum-exp weights of every split (one wavefront per sequence),
@@ -597,16 +708,16 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 //   3. the chunk's share of O~ W^u_v,h in float32 -> opj[jc][b][h][d].
 // W^u_v is read once per (chunk, head): the whole grid reads it once.
 template <typename PT, typename WT>
-__global__ __launch_bounds__(256) void merge_kernel(const PT *__restrict__ opart,
+__global__ __launch_bounds__(256) void merge_f32_kernel(const PT *__restrict__ opart,
                                                     const float *__restrict__ ml,
                                                     const WT *__restrict__ Wv,
                                                     const float *__restrict__ wscale,
                                                     float *__restrict__ opj, int b, int r,
                                                     int heads, int d, int S) {
   constexpr int BB = 16;
-  extern __shared__ float msm[];
-  float *wts = msm;                  // [BB][S]
-  float *mv = msm + BB * S;          // [BB][kMergeRows]
+  extern __shared__ float fsm[];
+  float *wts = fsm;                  // [BB][S]
+  float *mv = fsm + BB * S;          // [BB][kMergeRows]
   const int jc = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * BB;
   const int nbb = min(BB, b - b0);
   const int64_t E = static_cast<int64_t>(heads) * d;
@@ -731,46 +842,17 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__
     O[i] = acc;
 }
 
+
 // ------------------------------------------------------------------ dispatch helpers
-struct MfmaShape {
-  int W, nb, HGP, MAXNB, T;
-};
+constexpr size_t kMaxLds = 160 * 1024;
 
-// Register budget (256 VGPRs per lane at two wavefronts per SIMD): 32-head
-// groups up to 8 column blocks per wavefront, 16-head groups up to 18.
-MfmaShape mfma_shape(int r, int heads) {
-  MfmaShape s{};
-  s.W = 1;
-  for (int w : {8, 4, 2, 1})
-    if (r % (32 * w) == 0) {
-      s.W = w;
-      break;
-    }
-  s.nb = r / s.W / 16;
-  s.HGP = (heads > 16 && s.nb <= 8) ? 32 : 16;
-  s.MAXNB = 0;
-  const int cands32[] = {4, 8};
-  const int cands16[] = {4, 8, 12, 18};
-  if (s.HGP == 32) {
-    for (int c : cands32)
-      if (s.nb <= c) {
-        s.MAXNB = c;
-        break;
-      }
-  } else {
-    for (int c : cands16)
-      if (s.nb <= c) {
-        s.MAXNB = c;
-        break;
-      }
-  }
-  s.T = (s.MAXNB <= 12) ? 32 : 16;
-  return s;
-}
+// K blocks per 16-byte cache load for a cache dtype.
+int kpl_of(int c_dtype) { return c_dtype == QSVD_I4 ? 4 : (c_dtype == QSVD_I8 ? 2 : 1); }
 
-template <int CT, int HGP, int MAXNB, int T>
-hipError_t launch_stream_t(const StreamParams &sp, int W, size_t lds, hipStream_t s) {
-  auto kern = stream_mfma_kernel<CT, HGP, MAXNB, T>;
+template <int CT, int NHB, int NKB, int T>
+hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
+  auto kern = stream_mfma_kernel<CT, NHB, NKB, T>;
+  const size_t lds = stream_lds_bytes(W, NHB, NKB, T);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
@@ -779,18 +861,52 @@ hipError_t launch_stream_t(const StreamParams &sp, int W, size_t lds, hipStream_
   return hipGetLastError();
 }
 
+template <int CT, int NHB, int NKB>
+hipError_t launch_stream_tile(const StreamParams &sp, const MfmaShape &sh, hipStream_t s) {
+  if (sh.T == 32) return launch_stream_t<CT, NHB, NKB, 32>(sp, sh.W, s);
+  return launch_stream_t<CT, NHB, NKB, 16>(sp, sh.W, s);
+}
+
+template <int CT, int NKB>
+hipError_t launch_stream_nhb(const StreamParams &sp, const MfmaShape &sh, hipStream_t s) {
+  if constexpr (NKB <= 6) {
+    if (sh.NHB == 2) return launch_stream_tile<CT, 2, NKB>(sp, sh, s);
+  }
+  return launch_stream_tile<CT, 1, NKB>(sp, sh, s);
+}
+
 template <int CT>
 hipError_t launch_stream_ct(const StreamParams &sp, const MfmaShape &sh, hipStream_t s) {
-  const size_t lds = stream_lds_bytes(sh.W, sh.T, sh.nb * 16, sh.HGP);
-  if (sh.HGP == 32) {
-    if (sh.MAXNB == 4) return launch_stream_t<CT, 32, 4, 32>(sp, sh.W, lds, s);
-    return launch_stream_t<CT, 32, 8, 32>(sp, sh.W, lds, s);
-  }
-  switch (sh.MAXNB) {
-    case 4: return launch_stream_t<CT, 16, 4, 32>(sp, sh.W, lds, s);
-    case 8: return launch_stream_t<CT, 16, 8, 32>(sp, sh.W, lds, s);
-    case 12: return launch_stream_t<CT, 16, 12, 32>(sp, sh.W, lds, s);
-    default: return launch_stream_t<CT, 16, 18, 16>(sp, sh.W, lds, s);
+  if constexpr (CT == CT_BF16) {
+    switch (sh.NKB) {
+      case 1: return launch_stream_nhb<CT, 1>(sp, sh, s);
+      case 2: return launch_stream_nhb<CT, 2>(sp, sh, s);
+      case 3: return launch_stream_nhb<CT, 3>(sp, sh, s);
+      case 4: return launch_stream_nhb<CT, 4>(sp, sh, s);
+      case 5: return launch_stream_nhb<CT, 5>(sp, sh, s);
+      case 6: return launch_stream_nhb<CT, 6>(sp, sh, s);
+      case 7: return launch_stream_nhb<CT, 7>(sp, sh, s);
+      case 8: return launch_stream_nhb<CT, 8>(sp, sh, s);
+      case 9: return launch_stream_nhb<CT, 9>(sp, sh, s);
+      case 10: return launch_stream_nhb<CT, 10>(sp, sh, s);
+      case 11: return launch_stream_nhb<CT, 11>(sp, sh, s);
+      default: return launch_stream_nhb<CT, 12>(sp, sh, s);
+    }
+  } else if constexpr (CT == CT_I8) {
+    switch (sh.NKB) {
+      case 2: return launch_stream_nhb<CT, 2>(sp, sh, s);
+      case 4: return launch_stream_nhb<CT, 4>(sp, sh, s);
+      case 6: return launch_stream_nhb<CT, 6>(sp, sh, s);
+      case 8: return launch_stream_nhb<CT, 8>(sp, sh, s);
+      case 10: return launch_stream_nhb<CT, 10>(sp, sh, s);
+      default: return launch_stream_nhb<CT, 12>(sp, sh, s);
+    }
+  } else {
+    switch (sh.NKB) {
+      case 4: return launch_stream_nhb<CT, 4>(sp, sh, s);
+      case 8: return launch_stream_nhb<CT, 8>(sp, sh, s);
+      default: return launch_stream_nhb<CT, 12>(sp, sh, s);
+    }
   }
 }
 
@@ -830,12 +946,32 @@ hipError_t launch_absorb_t(const DecodeArgs &a, OT *qt, hipStream_t s) {
   }
 }
 
-template <typename PT, typename WT>
-hipError_t launch_merge_t(const DecodeArgs &a, const DecodePlan &p, const PT *opart,
-                          const float *ml, float *opj, hipStream_t s) {
+hipError_t launch_merge_f32(const DecodeArgs &a, const DecodePlan &p, const float *opart,
+                            const float *ml, float *opj, hipStream_t s) {
   const int JC = (a.r + kMergeRows - 1) / kMergeRows;
   const size_t lds = (static_cast<size_t>(16) * p.splits + 16 * kMergeRows) * sizeof(float);
-  auto kern = merge_kernel<PT, WT>;
+  auto kern = merge_f32_kernel<float, float>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
+      opart, ml, static_cast<const float *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
+      p.splits);
+  return hipGetLastError();
+}
+
+size_t merge_mfma_lds(int d, int S) {
+  return static_cast<size_t>(kMergeRows) * (d * 2 + 16) + (kMergeRows / 32) * 64 * 16 +
+         static_cast<size_t>(16) * S * sizeof(float);
+}
+
+template <typename WT>
+hipError_t launch_merge_mfma(const DecodeArgs &a, const DecodePlan &p, const uint16_t *opart,
+                             const float *ml, float *opj, hipStream_t s) {
+  const int JC = (a.r + kMergeRows - 1) / kMergeRows;
+  const size_t lds = merge_mfma_lds(a.d, p.splits);
+  auto kern = merge_mfma_kernel<WT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
@@ -859,24 +995,43 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
+// Shape of the MFMA stream kernel for a latent width r and cache dtype: the
+// largest wavefront count W <= 8 that gives every wavefront a whole number of
+// 16-byte loads per row (RW = r / W a multiple of 32 * KPL) with at most 12 K
+// blocks; two 16-head blocks per workgroup when at most 6 K blocks (register
+// budget), and 32-token tiles when they fit in LDS and registers (<= 10 K
+// blocks).
+bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
+  const int kpl = kpl_of(c_dtype);
+  for (int W = 8; W >= 1; --W) {
+    if (r % (W * 32 * kpl) != 0) continue;
+    const int nkb = r / (32 * W);
+    if (nkb > 12) return false;
+    MfmaShape s{};
+    s.W = W;
+    s.NKB = nkb;
+    s.NHB = (heads > 16 && nkb <= 6) ? 2 : 1;
+    s.T = (nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32) <= kMaxLds) ? 32 : 16;
+    if (stream_lds_bytes(W, s.NHB, nkb, s.T) > kMaxLds) return false;
+    if (out) *out = s;
+    return true;
+  }
+  return false;
+}
+
 DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, int splits) {
   DecodePlan p{};
   p.mfma = c_dtype != QSVD_F32;
-  int64_t tile = 32;
-  if (p.mfma) {
-    const MfmaShape sh = mfma_shape(r, heads);
-    tile = sh.T;
-    const int G = (heads + sh.HGP - 1) / sh.HGP;
-    p.head_groups = G;
-    p.group_heads = (heads + G - 1) / G;
-  } else {
-    p.head_groups = heads;
-    p.group_heads = 1;
-  }
   int64_t S;
   if (p.mfma) {
+    MfmaShape sh{};
+    mfma_shape(r, heads, c_dtype, &sh);  // validated by the caller
+    p.shape = sh;
+    const int G = (heads + 16 * sh.NHB - 1) / (16 * sh.NHB);
+    p.head_groups = G;
+    p.group_heads = (heads + G - 1) / G;
     // token tiles are dealt round-robin to the splits; no split is left empty
-    const int64_t tiles_all = (L + tile - 1) / tile;
+    const int64_t tiles_all = (L + sh.T - 1) / sh.T;
     if (splits > 0) {
       S = splits;
     } else {
@@ -887,6 +1042,8 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
     p.chunk = 0;
     p.splits = static_cast<int>(S);
   } else {
+    p.head_groups = heads;
+    p.group_heads = 1;
     const int64_t max_splits = std::min<int64_t>(kMaxSplits, L);
     if (splits > 0) {
       S = std::min<int64_t>(splits, max_splits);
@@ -956,7 +1113,7 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
       else if (maxj <= 16) e = run_stream_f32<16>(grid, lds, s, C, q, op, ml, a, p);
       else e = run_stream_f32<64>(grid, lds, s, C, q, op, ml, a, p);
     } else {
-      const MfmaShape sh = mfma_shape(a.r, a.heads);
+      const MfmaShape &sh = p.shape;
       StreamParams sp{};
       sp.C = static_cast<const uint8_t *>(a.C);
       sp.c_scales = a.c_scales;
@@ -967,10 +1124,8 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
       sp.r = a.r;
       sp.heads = a.heads;
       sp.S = p.splits;
-      sp.chunk = p.chunk;
       sp.G = p.head_groups;
       sp.group_heads = p.group_heads;
-      sp.nb = sh.nb;
       sp.ntasks = a.b * p.splits * p.head_groups;
       switch (a.c_dtype) {
         case QSVD_BF16: e = launch_stream_ct<CT_BF16>(sp, sh, s); break;
@@ -985,12 +1140,11 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
   {
     LaunchTimer t("decode_merge", s);
     if (!p.mfma)
-      e = launch_merge_t<float, float>(a, p, static_cast<const float *>(opart), ml, opj, s);
+      e = launch_merge_f32(a, p, static_cast<const float *>(opart), ml, opj, s);
     else if (a.wu_dtype == QSVD_I8)
-      e = launch_merge_t<uint16_t, int8_t>(a, p, static_cast<const uint16_t *>(opart), ml, opj, s);
+      e = launch_merge_mfma<int8_t>(a, p, static_cast<const uint16_t *>(opart), ml, opj, s);
     else
-      e = launch_merge_t<uint16_t, uint16_t>(a, p, static_cast<const uint16_t *>(opart), ml, opj,
-                                             s);
+      e = launch_merge_mfma<uint16_t>(a, p, static_cast<const uint16_t *>(opart), ml, opj, s);
     if (e != hipSuccess) return e;
   }
 

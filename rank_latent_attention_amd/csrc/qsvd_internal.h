@@ -64,8 +64,19 @@ struct DecodeArgs {
   void *workspace;
 };
 
+// Shape of the MFMA stream kernel: W wavefronts of RW = 32 NKB latent columns
+// each (r = W RW), NHB 16-head blocks per workgroup, T tokens per tile.
+struct MfmaShape {
+  int W, NKB, NHB, T;
+};
+
+// True when the MFMA stream kernel supports latent width r for the cache
+// dtype (bf16 / int8 / int4); fills *out (if non-NULL) with its shape.
+bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out);
+
 // Workspace layout of one decode call.
 struct DecodePlan {
+  MfmaShape shape;   // MFMA stream kernel shape (mfma only)
   int splits;        // L-splits per sequence
   int64_t chunk;     // tokens per split (multiple of the token tile)
   int head_groups;   // workgroups per (sequence, split) along heads

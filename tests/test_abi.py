@@ -130,7 +130,7 @@ def test_decode_validation():
 
 def test_workspace_and_splits_plan():
     # the default split count fills the 256 compute units once
-    assert q.qsvd_decode_default_splits(16, 8192, 1536, 32, 128, q.BF16) * 16 * 2 <= 256
+    assert q.qsvd_decode_default_splits(16, 8192, 1536, 32, 128, q.BF16) * 16 <= 256
     assert q.qsvd_decode_default_splits(8, 16384, 2304, 40, 128, q.BF16) == 10
     assert q.qsvd_decode_default_splits(1, 5, 256, 4, 64, q.BF16) == 1
     w1 = q.qsvd_decode_workspace_bytes(16, 8192, 1536, 32, 128, q.BF16, 1)
