@@ -116,16 +116,18 @@ __global__ __launch_bounds__(256) void absorb_kernel(const QT *__restrict__ q,
   }
 }
 
-// MFMA form for bf16 queries (d % 32 == 0): per head, Q~_h[b][j] = q_h[b][:] . W^u_k[j][h d:(h+1) d]
-// is a [16 sequences x d] x [d x 16 rows] product per v_mfma_f32_16x16x32_bf16
-// chain.  Workgroup = (64 rows j, head h, 16 sequences); wavefront = 16 rows.
-// int8 W^u_k codes convert exactly to bf16; their column scales multiply q.
-template <typename WT>
+// MFMA form for bf16 queries (d = 32 DK): per head, Q~_h[b][j] = q_h[b][:] . W^u_k[j][h d:(h+1) d]
+// is a [16 sequences x d] x [d x 16 rows] product, DK v_mfma_f32_16x16x32_bf16
+// steps.  Workgroup = (64 rows j, head h, 16 sequences); wavefront = 16 rows.
+// All operand loads are issued before the first product.  int8 W^u_k codes
+// convert exactly to bf16; their column scales multiply q.
+template <typename WT, int DK>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__restrict__ q,
                                                           const WT *__restrict__ Wk,
                                                           const float *__restrict__ wscale,
                                                           uint16_t *__restrict__ qt, int b, int r,
-                                                          int heads, int d, float scale) {
+                                                          int heads, float scale) {
+  constexpr int d = 32 * DK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.y, b0 = blockIdx.z * 16;
   const int j0 = blockIdx.x * 64 + wave * 16;
@@ -133,38 +135,46 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
   const int bb = b0 + (lane & 15);
   const int j = j0 + (lane & 15);
   const int kq = (lane >> 4) * 8;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    const int i = k0 + kq;
-    u32x4 av = {0u, 0u, 0u, 0u}, bv = {0u, 0u, 0u, 0u};
-    if (bb < b) {
-      av = *reinterpret_cast<const u32x4 *>(q + (static_cast<int64_t>(bb) * heads + h) * d + i);
-      if (wscale) {
+  u32x4 av[DK], bv[DK];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(av[e] << 16) * wscale[h * d + i + 2 * e];
-          const float hi = __uint_as_float(av[e] & 0xFFFF0000u) * wscale[h * d + i + 2 * e + 1];
-          av[e] = pack_bf16x2(lo, hi);
-        }
-      }
-    }
+  for (int k = 0; k < DK; ++k) {
+    const int i = 32 * k + kq;
+    av[k] = u32x4{0u, 0u, 0u, 0u};
+    bv[k] = u32x4{0u, 0u, 0u, 0u};
+    if (bb < b) av[k] = *reinterpret_cast<const u32x4 *>(q + (static_cast<int64_t>(bb) * heads + h) * d + i);
     if (j < r) {
       if constexpr (sizeof(WT) == 2) {
-        bv = *reinterpret_cast<const u32x4 *>(Wk + static_cast<int64_t>(j) * E + h * d + i);
+        bv[k] = *reinterpret_cast<const u32x4 *>(Wk + static_cast<int64_t>(j) * E + h * d + i);
       } else {
         const u32x2 c = *reinterpret_cast<const u32x2 *>(Wk + static_cast<int64_t>(j) * E + h * d + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t word = c[e >> 1];
-          const int sh = 16 * (e & 1);
-          const int c0 = static_cast<int>(word << (24 - sh)) >> 24;
-          const int c1 = static_cast<int>(word << (16 - sh)) >> 24;
-          bv[e] = pack_bf16x2(static_cast<float>(c0), static_cast<float>(c1));
-        }
+        bv[k] = u32x4{c.x, c.y, 0u, 0u};
       }
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                  __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < DK; ++k) {
+    const int i = 32 * k + kq;
+    u32x4 a = av[k], w = bv[k];
+    if (wscale) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(a[e] << 16) * wscale[h * d + i + 2 * e];
+        const float hi = __uint_as_float(a[e] & 0xFFFF0000u) * wscale[h * d + i + 2 * e + 1];
+        a[e] = pack_bf16x2(lo, hi);
+      }
+    }
+    if constexpr (sizeof(WT) == 1) {
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const uint32_t word = w[e >> 1];
+        const int sh = 16 * (e & 1);
+        w[e] = pack_bf16x2(static_cast<float>(static_cast<int>(word << (24 - sh)) >> 24),
+                           static_cast<float>(static_cast<int>(word << (16 - sh)) >> 24));
+      }
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, w), acc, 0, 0, 0);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -288,11 +298,14 @@ struct CacheTraits<CT_I4> {
 };
 
 __host__ __device__ constexpr int ct_row_stride(int nkb) { return nkb * 64 + 16; }
+// partial scores of one wavefront: [NHB * 16 heads][T + 4] float32 (head-major,
+// padded so that the 16 heads of one store land in distinct LDS banks)
+__host__ __device__ constexpr int sp_row(int T) { return T + 4; }
 
 // LDS bytes of the stream kernel: wavefront C tiles | partial scores | P | alpha, m, l.
 __host__ __device__ constexpr size_t stream_lds_bytes(int W, int NHB, int NKB, int T) {
   return static_cast<size_t>(W) * T * ct_row_stride(NKB) +
-         static_cast<size_t>(W) * (T / 16) * NHB * 64 * 16 + static_cast<size_t>(NHB) * 64 * T / 2 +
+         static_cast<size_t>(W) * NHB * 16 * sp_row(T) * 4 + static_cast<size_t>(NHB) * 64 * T / 2 +
          static_cast<size_t>(NHB) * 16 * 4 * 3;
 }
 
@@ -305,15 +318,45 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t *p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// bf16 pair of two float32 values, hardware round-to-nearest-even conversion.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // bf16 pair of two dequantised codes c * s (float32 product, round to nearest even).
 __device__ __forceinline__ uint32_t dq_pair(int c0, int c1, float s) {
-  return pack_bf16x2(static_cast<float>(c0) * s, static_cast<float>(c1) * s);
+  return cvt_bf16x2(static_cast<float>(c0) * s, static_cast<float>(c1) * s);
+}
+
+// Reductions over aligned groups of N = 8 or 16 lanes with DPP lane swaps
+// (xor 1, xor 2, mirror within 8, mirror within 16).
+template <int CTRL, bool MAX>
+__device__ __forceinline__ float dpp_step(float x) {
+  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return MAX ? fmaxf(x, y) : x + y;
+}
+
+template <int N, bool MAX>
+__device__ __forceinline__ float dpp_reduce(float v) {
+  v = dpp_step<0xB1, MAX>(v);   // quad_perm [1,0,3,2]
+  v = dpp_step<0x4E, MAX>(v);   // quad_perm [2,3,0,1]
+  v = dpp_step<0x141, MAX>(v);  // row_half_mirror
+  if constexpr (N == 16) v = dpp_step<0x140, MAX>(v);  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(n), 0x00020000);
 }
 
 // Template parameters: cache format CT, NHB 16-head blocks per workgroup, NKB
 // 32-column K blocks per wavefront (RW = 32 NKB columns), T tokens per tile
 // (32, or 16 when a 32-token tile does not fit in LDS).  The wavefront count
-// W = blockDim.x / 64 satisfies r = W * RW.
+// W = blockDim.x / 64 <= 8 satisfies r = W * RW.
 template <int CT, int NHB, int NKB, int T>
 __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   using Tr = CacheTraits<CT>;
@@ -325,8 +368,12 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   constexpr int RW = NKB * 32;          // columns per wavefront
   constexpr int RS = ct_row_stride(NKB);
   constexpr int PPL = T / 4;            // P elements per lane (value-product A operand)
+  constexpr int SPR = sp_row(T);
+  constexpr int HGP = NHB * 16;
+  constexpr int MAXW = 8;
   static_assert(NKB % KPL == 0, "wavefront columns must be whole 16-byte loads");
   static_assert(T == 16 || T == 32, "tile");
+  static_assert(HGP * RW * 2 <= T * RS, "the output rows are staged in the wavefront's C tile");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -358,11 +405,46 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   const int j0w = wave * RW;
 
   uint8_t *ct = smem + static_cast<size_t>(wave) * T * RS;
-  f32x4 *spart = reinterpret_cast<f32x4 *>(smem + static_cast<size_t>(W) * T * RS);
-  uint16_t *pl = reinterpret_cast<uint16_t *>(spart + static_cast<size_t>(W) * NTB * NHB * 64);
+  float *spart = reinterpret_cast<float *>(smem + static_cast<size_t>(W) * T * RS);
+  uint16_t *pl = reinterpret_cast<uint16_t *>(spart + static_cast<size_t>(W) * HGP * SPR);
   float *alpha_s = reinterpret_cast<float *>(pl + NHB * 64 * PPL);
-  float *m_s = alpha_s + NHB * 16;
-  float *l_s = m_s + NHB * 16;
+  float *m_s = alpha_s + HGP;
+  float *l_s = m_s + HGP;
+
+  // ---- tile loads through buffer resources based at the tile's first row:
+  // rows at or past the end of the sequence fall outside the resource and
+  // read as zero (their scores are masked to -inf below, so their P is 0).
+  const int64_t row_bytes = Tr::byte_offset(r);
+  const uint32_t voff0 = static_cast<uint32_t>(li * row_bytes + Tr::byte_offset(j0w + EPL * lg));
+  u32x4 stage[NTB][NLD];
+  float sscale[NTB][NLD];
+  auto load_rows = [&](int64_t t0, int tb) {
+    const int64_t row0 = static_cast<int64_t>(seq) * L + t0;
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(p.C + row0 * row_bytes, (L - t0) * row_bytes);
+    const uint32_t vo = voff0 + static_cast<uint32_t>(tb * 16 * row_bytes);
+#pragma unroll
+    for (int ld = 0; ld < NLD; ++ld)
+      stage[tb][ld] = __builtin_amdgcn_raw_buffer_load_b128(rc, vo + ld * Tr::byte_offset(32 * KPL), 0, 0);
+    if constexpr (CT == CT_I8) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.c_scales + row0, (L - t0) * 4);
+      const float sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (tb * 16 + li) * 4, 0, 0));
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld) sscale[tb][ld] = sc;
+    }
+    if constexpr (CT == CT_I4) {
+      const int groups = r / 128;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.c_scales + row0 * groups, (L - t0) * groups * 4);
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld)
+        sscale[tb][ld] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, ((tb * 16 + li) * groups + (j0w + 128 * ld) / 128) * 4, 0, 0));
+    }
+  };
+
+  if (ntiles > 0) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) load_rows(static_cast<int64_t>(split) * T, tb);
+  }
 
   // Absorbed queries as the B operand of the score product.  K block
   // kb = KPL * ld + s of lane group g covers columns
@@ -389,32 +471,11 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[hb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int i = tid; i < NHB * 16; i += nthreads) {
+  for (int i = tid; i < HGP; i += nthreads) {
     m_s[i] = -INFINITY;
     l_s[i] = 0.f;
   }
 
-  // ---- tile loads: row block tb, load ld -> stage[tb][ld]
-  u32x4 stage[NTB][NLD];
-  float sscale[NTB][NLD];
-  const int64_t row_base = static_cast<int64_t>(seq) * L;
-  auto load_rows = [&](int64_t t0, int tb) {
-    // rows past the end of the sequence re-read its last row; their scores
-    // are masked to -inf below, so their P is 0
-    const int64_t tok = row_base + min(t0 + tb * 16 + li, L - 1);
-#pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) {
-      const int64_t col = j0w + 32 * KPL * ld + EPL * lg;
-      stage[tb][ld] = *reinterpret_cast<const u32x4 *>(p.C + Tr::byte_offset(tok * r + col));
-      if constexpr (CT == CT_I8) sscale[tb][ld] = p.c_scales[tok];
-      if constexpr (CT == CT_I4) sscale[tb][ld] = p.c_scales[tok * (r / 128) + col / 128];
-    }
-  };
-
-  if (ntiles > 0) {
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) load_rows(static_cast<int64_t>(split) * T, tb);
-  }
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
@@ -424,7 +485,6 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 
     // ---- 1-3. per 16-token row block: bf16 A operands, partial scores over
     // this wavefront's columns, the rows to LDS, then the next tile's loads
-    f32x4 sacc[NTB][NHB];
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       u32x4 cv[NKB];
@@ -459,14 +519,15 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
           }
         }
       }
+      f32x4 sacc[NHB];
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) sacc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int hb = 0; hb < NHB; ++hb) sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb)
-          sacc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, cv[kb]), qf[hb][kb], sacc[tb][hb], 0, 0, 0);
+          sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, cv[kb]), qf[hb][kb], sacc[hb], 0, 0, 0);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int ld = kb / KPL, s = kb % KPL;
@@ -474,54 +535,58 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         *reinterpret_cast<u32x4 *>(ct + (tb * 16 + li) * RS + jl * 2) = cv[kb];
       }
       if (more) load_rows(next_t0, tb);
+      // partial scores, head-major: lane holds tokens 16 tb + 4 g + (0..3) of head 16 hb + i
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        *reinterpret_cast<f32x4 *>(spart + (wave * HGP + hb * 16 + li) * SPR + tb * 16 + 4 * lg) = sacc[hb];
     }
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) spart[((wave * NTB + tb) * NHB + hb) * 64 + lane] = sacc[tb][hb];
     __syncthreads();
 
     // ---- 4. cross-wavefront sum + online softmax; T/2 lanes per head, 2 tokens each
-    for (int item = tid; item < NHB * 16 * (T / 2); item += nthreads) {
+    for (int item = tid; item < HGP * (T / 2); item += nthreads) {
       const int h = item / (T / 2), u = item % (T / 2), t0 = 2 * u;
-      const int tb = t0 >> 4, hb = h >> 4;
-      const int ln = 16 * ((t0 & 15) >> 2) + (h & 15);
-      const int e0 = t0 & 3;
       float s0 = 0.f, s1 = 0.f;
-      for (int w = 0; w < W; ++w) {
-        const float *src = reinterpret_cast<const float *>(spart + ((w * NTB + tb) * NHB + hb) * 64 + ln);
-        const float2 v = *reinterpret_cast<const float2 *>(src + e0);
-        s0 += v.x;
-        s1 += v.y;
+      // all MAXW reads in flight: rows past W re-read row W-1 and add nothing
+      float2 v[MAXW];
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w)
+        v[w] = *reinterpret_cast<const float2 *>(spart + (min(w, W - 1) * HGP + h) * SPR + t0);
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) {
+        s0 += (w < W) ? v[w].x : 0.f;
+        s1 += (w < W) ? v[w].y : 0.f;
       }
       if (tile_t0 + t0 >= L) s0 = -INFINITY;
       if (tile_t0 + t0 + 1 >= L) s1 = -INFINITY;
-      const float mx = group_max<T / 2>(fmaxf(s0, s1));
+      const float mx = dpp_reduce<T / 2, true>(fmaxf(s0, s1));
       const float m_old = m_s[h];
       const float m_new = fmaxf(m_old, mx);
-      const float alpha = exp2f(m_old - m_new);
-      const uint16_t p0 = f32_to_bf16(exp2f(s0 - m_new));
-      const uint16_t p1 = f32_to_bf16(exp2f(s1 - m_new));
-      const float psum = group_sum<T / 2>(bf16_to_f32(p0) + bf16_to_f32(p1));
+      const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
+      const uint32_t pp = cvt_bf16x2(__builtin_amdgcn_exp2f(s0 - m_new), __builtin_amdgcn_exp2f(s1 - m_new));
+      const float psum = dpp_reduce<T / 2, false>(__uint_as_float(pp << 16) + __uint_as_float(pp & 0xFFFF0000u));
       if (u == 0) {
         m_s[h] = m_new;
         l_s[h] = fmaf(l_s[h], alpha, psum);
         alpha_s[h] = alpha;
       }
       // P as the A operand of the value product: lane 16 (t / PPL) + h % 16, element t % PPL
-      uint16_t *pdst = pl + (hb * 64 + 16 * (t0 / PPL) + (h & 15)) * PPL + (t0 % PPL);
-      *reinterpret_cast<uint32_t *>(pdst) = static_cast<uint32_t>(p0) | (static_cast<uint32_t>(p1) << 16);
+      uint16_t *pdst = pl + ((h >> 4) * 64 + 16 * (t0 / PPL) + (h & 15)) * PPL + (t0 % PPL);
+      *reinterpret_cast<uint32_t *>(pdst) = pp;
     }
     __syncthreads();
 
-    // ---- 5. O~ = O~ * alpha + P^T C_tile
+    // ---- 5. O~ = O~ * alpha + P^T C_tile (the rescale is skipped by a
+    // wavefront whose heads all kept their running maximum)
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const f32x4 al = *reinterpret_cast<const f32x4 *>(alpha_s + hb * 16 + 4 * lg);
+      const bool keep = al[0] == 1.f && al[1] == 1.f && al[2] == 1.f && al[3] == 1.f;
+      if (__builtin_amdgcn_ballot_w64(!keep) != 0) {
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb)
+        for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[hb][jb][e] *= al[e];
+          for (int e = 0; e < 4; ++e) oacc[hb][jb][e] *= al[e];
+      }
     }
     // B operand: tokens PPL g + (0..PPL-1) of column 16 jb + lane % 16, by
     // transposing 8-byte reads of 4 tokens each (lane i of a 16-lane group
@@ -557,21 +622,30 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   }
   __syncthreads();
 
-  // ---- partial state: O~ / l (bf16) and (m, l)
+  // ---- partial state: O~ / l (bf16, [head][RW] rows staged in this
+  // wavefront's LDS tile, then 16-byte stores) and (m, l)
   const int64_t pbase = (static_cast<int64_t>(seq) * p.S + split) * p.heads + h0;
+  {
+    uint16_t *ot = reinterpret_cast<uint16_t *>(ct);  // [HGP][RW]; HGP * RW * 2 <= T * RS
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
+    for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = hb * 16 + 4 * lg + e;
-      if (h < hg) {
+      for (int e = 0; e < 4; ++e) {
+        const int h = hb * 16 + 4 * lg + e;
         const float l = l_s[h];
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t *dst = p.opart + (pbase + h) * r + j0w + li;
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) dst[jb * 16] = f32_to_bf16(oacc[hb][jb][e] * inv);
+        for (int jb = 0; jb < NJB; ++jb) ot[h * RW + jb * 16 + li] = f32_to_bf16(oacc[hb][jb][e] * inv);
       }
+    // same-wavefront LDS write -> read: ordered by the LDS queue
+    constexpr int UPR = RW / 8;  // 16-byte units per head row
+    for (int u = lane; u < HGP * UPR; u += 64) {
+      const int h = u / UPR, c8 = (u % UPR) * 8;
+      if (h < hg)
+        *reinterpret_cast<u32x4 *>(p.opart + (pbase + h) * r + j0w + c8) =
+            *reinterpret_cast<const u32x4 *>(ot + h * RW + c8);
     }
+  }
   for (int h = tid; h < hg; h += nthreads) {
     p.ml[2 * (pbase + h)] = m_s[h];
     p.ml[2 * (pbase + h) + 1] = l_s[h];
@@ -580,15 +654,18 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 
 // ------------------------------------------------------------------ MFMA merge
 // Workgroup (chunk jc of kMergeRows latent rows, head h, 16 sequences):
-//   1. log-sum-exp weights of every split (one wavefront per sequence);
-//   2. merged O~ rows of the chunk (8 rows per thread, 16-byte partial
-//      loads), written to LDS as the A operand of v_mfma_f32_16x16x32_bf16
-//      (M = 16 sequences, K = latent rows);
-//   3. the chunk of W^u_v,h (kMergeRows x d) to LDS as bf16 (int8 codes are
-//      exact in bf16; their column scales multiply the result);
+//   1. the chunk of W^u_v,h (kMergeRows x d) is fetched into registers (int8
+//      codes are exact in bf16; their column scales multiply the result);
+//   2. log-sum-exp weights of every split (16 lanes per sequence);
+//   3. merged O~ rows of the chunk (8 rows per thread, the partial loads of 8
+//      splits in flight at once), written to LDS as the A operand of
+//      v_mfma_f32_16x16x32_bf16 (M = 16 sequences, K = latent rows);
 //   4. O~ W^u_v,h with the B operand read by transposing LDS loads ->
 //      opj[jc][b][h][:] (float32).
-// W^u_v is read once per (chunk, head, 16 sequences).
+// W^u_v is read once per (chunk, head, 16 sequences).  A device-scope fence
+// per workgroup to let the last chunk sum the shares costs more than a
+// separate finalize launch (the release writes back the L2), so the shares
+// are summed by decode_finalize.
 template <typename WT>
 __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restrict__ opart,
                                                          const float *__restrict__ ml,
@@ -597,6 +674,7 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
                                                          float *__restrict__ opj, int b, int r,
                                                          int heads, int d, int S) {
   constexpr int BB = 16;
+  constexpr int MAXU = kMergeRows * 256 / 8 / 256;  // 8-column W units per thread (d <= 256)
   extern __shared__ __attribute__((aligned(16))) uint8_t msm[];
   const int WRS = d * 2 + 16;                                       // W chunk row stride (bytes)
   uint8_t *wl = msm;                                                // [kMergeRows][WRS]
@@ -608,39 +686,56 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
   const int j0 = jc * kMergeRows;
   const int rows = min(kMergeRows, r - j0);  // multiple of 32
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int units = d / 8;                   // 8-column units per row
 
-  // 1. split weights
-  for (int bi = wave; bi < nbb; bi += 4) {
-    const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
+  // 1. W^u_v chunk -> registers
+  u32x4 wreg[MAXU];
+#pragma unroll
+  for (int k = 0; k < MAXU; ++k) {
+    const int u = tid + 256 * k;
+    wreg[k] = u32x4{0u, 0u, 0u, 0u};
+    if (u < rows * units) {
+      const int row = u / units, c8 = (u % units) * 8;
+      const WT *src = Wv + static_cast<int64_t>(j0 + row) * E + static_cast<int64_t>(h) * d + c8;
+      if constexpr (sizeof(WT) == 2) {
+        wreg[k] = *reinterpret_cast<const u32x4 *>(src);
+      } else {
+        const u32x2 c = *reinterpret_cast<const u32x2 *>(src);
+        wreg[k] = u32x4{c.x, c.y, 0u, 0u};
+      }
+    }
+  }
+
+  // 2. split weights: thread (sequence tid / 16, splits tid % 16, +16, ...)
+  {
+    const int bi = tid >> 4, sl = tid & 15;
+    const int64_t base = static_cast<int64_t>(b0 + min(bi, nbb - 1)) * S * heads + h;
     float mx = -INFINITY;
-    for (int s = lane; s < S; s += 64) mx = fmaxf(mx, ml[2 * (base + static_cast<int64_t>(s) * heads)]);
-    mx = group_max<64>(mx);
+    for (int s = sl; s < S; s += 16) mx = fmaxf(mx, ml[2 * (base + static_cast<int64_t>(s) * heads)]);
+    mx = group_max<16>(mx);
     float den = 0.f;
-    for (int s = lane; s < S; s += 64) {
+    for (int s = sl; s < S; s += 16) {
       const int64_t o = base + static_cast<int64_t>(s) * heads;
       const float w = (mx == -INFINITY) ? 0.f : exp2f(ml[2 * o] - mx) * ml[2 * o + 1];
       wts[bi * S + s] = w;
       den += w;
     }
-    den = group_sum<64>(den);
+    den = group_sum<16>(den);
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int s = lane; s < S; s += 64) wts[bi * S + s] *= inv;
+    for (int s = sl; s < S; s += 16) wts[bi * S + s] *= inv;
   }
 
-  // 3. W^u_v chunk -> LDS (bf16), 16 output bytes per thread per pass
-  {
-    const int units = d / 8;  // 16-byte bf16 units per row
-    for (int u = tid; u < rows * units; u += 256) {
-      const int row = u / units, c8 = (u % units) * 8;
-      const WT *src = Wv + static_cast<int64_t>(j0 + row) * E + static_cast<int64_t>(h) * d + c8;
-      u32x4 v;
-      if constexpr (sizeof(WT) == 2) {
-        v = *reinterpret_cast<const u32x4 *>(src);
-      } else {
-        const u32x2 c = *reinterpret_cast<const u32x2 *>(src);
+  // W registers -> LDS (bf16)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t word = c[e >> 1];
+  for (int k = 0; k < MAXU; ++k) {
+    const int u = tid + 256 * k;
+    if (u < rows * units) {
+      const int row = u / units, c8 = (u % units) * 8;
+      u32x4 v = wreg[k];
+      if constexpr (sizeof(WT) == 1) {
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          const uint32_t word = v[e >> 1];
           const int sh = 16 * (e & 1);
           v[e] = pack_bf16x2(static_cast<float>(static_cast<int>(word << (24 - sh)) >> 24),
                              static_cast<float>(static_cast<int>(word << (16 - sh)) >> 24));
@@ -651,22 +746,28 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
   }
   __syncthreads();
 
-  // 2. merged O~ rows: thread (sequence tid / 16, rows 8 (tid % 16) .. +8)
+  // 3. merged O~ rows: thread (sequence tid / 16, rows 8 (tid % 16) .. +8)
   {
     const int bi = tid >> 4, jj0 = (tid & 15) * 8;
+    const bool valid = bi < nbb && jj0 < rows;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (bi < nbb && jj0 < rows) {
-      const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
-      for (int s = 0; s < S; ++s) {
-        const float w = wts[bi * S + s];
-        if (w != 0.f) {
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(
-              opart + (base + static_cast<int64_t>(s) * heads) * r + j0 + jj0);
+    const int64_t base = static_cast<int64_t>(b0 + min(bi, nbb - 1)) * S * heads + h;
+    const uint16_t *src = opart + base * r + j0 + min(jj0, rows - 8);
+    const int64_t sstride = static_cast<int64_t>(heads) * r;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      u32x4 v[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
-            acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xFFFF0000u), acc[2 * e + 1]);
-          }
+      for (int k = 0; k < 8; ++k) {
+        v[k] = u32x4{0u, 0u, 0u, 0u};
+        if (valid && s0 + k < S) v[k] = *reinterpret_cast<const u32x4 *>(src + (s0 + k) * sstride);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = (s0 + k < S) ? wts[bi * S + s0 + k] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(w, __uint_as_float(v[k][e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w, __uint_as_float(v[k][e] & 0xFFFF0000u), acc[2 * e + 1]);
         }
       }
     }
@@ -698,8 +799,8 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
       if (bi < nbb) opj[((static_cast<int64_t>(jc) * b + b0 + bi) * heads + h) * d + col] = acc[e] * sc;
     }
   }
-}
 
+}
 
 // ------------------------------------------------------------------ merge
 // Workgroup (chunk jc of 128 latent rows, head h, 16 sequences):
@@ -829,19 +930,29 @@ __global__ __launch_bounds__(256) void merge_f32_kernel(const PT *__restrict__ o
   }
 }
 
+// O = sum over the JC chunk shares, 4 consecutive outputs per thread, the
+// loads of all chunks issued before the sum (n % 4 == 0).
 template <typename OT>
 __global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ opj,
                                                        OT *__restrict__ O, int64_t n, int JC) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  constexpr int MAXJC = 32;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
-  float acc = 0.f;
-  for (int jc = 0; jc < JC; ++jc) acc += opj[static_cast<int64_t>(jc) * n + i];
-  if constexpr (sizeof(OT) == 2)
-    O[i] = f32_to_bf16(acc);
-  else
-    O[i] = acc;
+  f32x4 v[MAXJC];
+#pragma unroll
+  for (int c = 0; c < MAXJC; ++c)
+    if (c < JC) v[c] = *reinterpret_cast<const f32x4 *>(opj + c * n + i);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < MAXJC; ++c)
+    if (c < JC) acc += v[c];
+  for (int c = MAXJC; c < JC; ++c) acc += *reinterpret_cast<const f32x4 *>(opj + c * n + i);
+  if constexpr (sizeof(OT) == 2) {
+    *reinterpret_cast<u32x2 *>(O + i) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  } else {
+    *reinterpret_cast<f32x4 *>(O + i) = acc;
+  }
 }
-
 
 // ------------------------------------------------------------------ dispatch helpers
 constexpr size_t kMaxLds = 160 * 1024;
@@ -863,8 +974,12 @@ hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
 
 template <int CT, int NHB, int NKB>
 hipError_t launch_stream_tile(const StreamParams &sp, const MfmaShape &sh, hipStream_t s) {
-  if (sh.T == 32) return launch_stream_t<CT, NHB, NKB, 32>(sp, sh.W, s);
-  return launch_stream_t<CT, NHB, NKB, 16>(sp, sh.W, s);
+  if constexpr (NHB == 2) {
+    return launch_stream_t<CT, NHB, NKB, 32>(sp, sh.W, s);  // mfma_shape pairs NHB = 2 with T = 32
+  } else {
+    if (sh.T == 32) return launch_stream_t<CT, NHB, NKB, 32>(sp, sh.W, s);
+    return launch_stream_t<CT, NHB, NKB, 16>(sp, sh.W, s);
+  }
 }
 
 template <int CT, int NKB>
@@ -982,13 +1097,23 @@ hipError_t launch_merge_mfma(const DecodeArgs &a, const DecodePlan &p, const uin
   return hipGetLastError();
 }
 
+template <typename WT, int DK>
+hipError_t launch_absorb_mfma_t(const DecodeArgs &a, uint16_t *qt, hipStream_t s) {
+  const dim3 grid((a.r + 63) / 64, a.heads, (a.b + 15) / 16);
+  absorb_mfma_kernel<WT, DK><<<grid, dim3(256), 0, s>>>(
+      static_cast<const uint16_t *>(a.q), static_cast<const WT *>(a.Wu_k), a.wu_scale_k, qt, a.b,
+      a.r, a.heads, a.softmax_scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <typename WT>
 hipError_t launch_absorb_mfma(const DecodeArgs &a, uint16_t *qt, hipStream_t s) {
-  const dim3 grid((a.r + 63) / 64, a.heads, (a.b + 15) / 16);
-  absorb_mfma_kernel<WT><<<grid, dim3(256), 0, s>>>(
-      static_cast<const uint16_t *>(a.q), static_cast<const WT *>(a.Wu_k), a.wu_scale_k, qt, a.b,
-      a.r, a.heads, a.d, a.softmax_scale * kLog2e);
-  return hipGetLastError();
+  switch (a.d) {
+    case 32: return launch_absorb_mfma_t<WT, 1>(a, qt, s);
+    case 64: return launch_absorb_mfma_t<WT, 2>(a, qt, s);
+    case 128: return launch_absorb_mfma_t<WT, 4>(a, qt, s);
+    default: return launch_absorb_mfma_t<WT, 8>(a, qt, s);
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1010,7 +1135,7 @@ bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
     MfmaShape s{};
     s.W = W;
     s.NKB = nkb;
-    s.NHB = (heads > 16 && nkb <= 6) ? 2 : 1;
+    s.NHB = (heads > 16 && nkb <= 6 && stream_lds_bytes(W, 2, nkb, 32) <= kMaxLds) ? 2 : 1;
     s.T = (nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32) <= kMaxLds) ? 32 : 16;
     if (stream_lds_bytes(W, s.NHB, nkb, s.T) > kMaxLds) return false;
     if (out) *out = s;
@@ -1153,7 +1278,7 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
     LaunchTimer t("decode_finalize", s);
     const int64_t n = static_cast<int64_t>(a.b) * a.heads * a.d;
     const int JC = (a.r + kMergeRows - 1) / kMergeRows;
-    const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
+    const dim3 grid(static_cast<unsigned>((n / 4 + 255) / 256)), block(256);
     if (a.o_dtype == QSVD_BF16)
       finalize_kernel<uint16_t><<<grid, block, 0, s>>>(opj, static_cast<uint16_t *>(a.O), n, JC);
     else
