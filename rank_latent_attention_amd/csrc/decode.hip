@@ -42,6 +42,8 @@
 #include "qsvd_internal.h"
 
 #include <cmath>
+#include <cstdlib>
+#include <type_traits>
 
 namespace qsvd {
 namespace {
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(const QT *__restrict__ q,
 }
 
 // MFMA form for bf16 queries (d = 32 DK): per head, Q~_h[b][j] = q_h[b][:] . W^u_k[j][h d:(h+1) d]
-// is a [16 sequences x d] x [d x 16 rows] product, DK v_mfma_f32_16x16x32_bf16
-// steps.  Workgroup = (64 rows j, head h, 16 sequences); wavefront = 16 rows.
+// is computed transposed, [16 rows x d] x [d x 16 sequences], DK
+// v_mfma_f32_16x16x32_bf16 steps.  Workgroup = (64 rows j, head h, 16 sequences); wavefront = 16 rows.
 // All operand loads are issued before the first product.  int8 W^u_k codes
 // convert exactly to bf16; their column scales multiply q.
 template <typename WT, int DK>
@@ -173,14 +175,15 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
                            static_cast<float>(static_cast<int>(word << (16 - sh)) >> 24));
       }
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, w), acc, 0, 0, 0);
+    // transposed product: rows j of W^u_k as A, sequences as B, so that a
+    // lane ends with 4 consecutive rows j0 + 4 g + (0..3) of sequence b0 + i
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                  __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int bo = b0 + 4 * (lane >> 4) + e;
-    if (bo < b && j < r) qt[(static_cast<int64_t>(bo) * heads + h) * r + j] = f32_to_bf16(acc[e] * scale);
-  }
+  const int jo = j0 + 4 * (lane >> 4);
+  if (bb < b && jo < r)  // r % 16 == 0: the 4 rows are all valid
+    *reinterpret_cast<u32x2 *>(qt + (static_cast<int64_t>(bb) * heads + h) * r + jo) =
+        u32x2{pack_bf16x2(acc[0] * scale, acc[1] * scale), pack_bf16x2(acc[2] * scale, acc[3] * scale)};
 }
 
 // ------------------------------------------------------------------ float32 stream
@@ -355,9 +358,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 
 // Template parameters: cache format CT, NHB 16-head blocks per workgroup, NKB
 // 32-column K blocks per wavefront (RW = 32 NKB columns), T tokens per tile
-// (32, or 16 when a 32-token tile does not fit in LDS).  The wavefront count
-// W = blockDim.x / 64 <= 8 satisfies r = W * RW.
-template <int CT, int NHB, int NKB, int T>
+// (32 or 16), D tiles of loads in flight (1 or 2; register staging).  The
+// wavefront count W = blockDim.x / 64 <= 8 satisfies r = W * RW.
+template <int CT, int NHB, int NKB, int T, int D>
 __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   using Tr = CacheTraits<CT>;
   constexpr int EPL = Tr::EPL;
@@ -367,12 +370,13 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   constexpr int NJB = NKB * 2;          // 16-column blocks of O~
   constexpr int RW = NKB * 32;          // columns per wavefront
   constexpr int RS = ct_row_stride(NKB);
-  constexpr int PPL = T / 4;            // P elements per lane (value-product A operand)
+  constexpr int PPL = T / 4;            // tokens per lane in the value product operands
   constexpr int SPR = sp_row(T);
   constexpr int HGP = NHB * 16;
   constexpr int MAXW = 8;
   static_assert(NKB % KPL == 0, "wavefront columns must be whole 16-byte loads");
   static_assert(T == 16 || T == 32, "tile");
+  static_assert(D == 1 || D == 2, "prefetch depth");
   static_assert(HGP * RW * 2 <= T * RS, "the output rows are staged in the wavefront's C tile");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -416,34 +420,41 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   // read as zero (their scores are masked to -inf below, so their P is 0).
   const int64_t row_bytes = Tr::byte_offset(r);
   const uint32_t voff0 = static_cast<uint32_t>(li * row_bytes + Tr::byte_offset(j0w + EPL * lg));
-  u32x4 stage[NTB][NLD];
-  float sscale[NTB][NLD];
-  auto load_rows = [&](int64_t t0, int tb) {
+  u32x4 stage[D][NTB][NLD];
+  float sscale[D][NTB][NLD];
+  auto load_rows = [&](auto BUF, int64_t t0, int tb) {
+    constexpr int bf = decltype(BUF)::value;
     const int64_t row0 = static_cast<int64_t>(seq) * L + t0;
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(p.C + row0 * row_bytes, (L - t0) * row_bytes);
     const uint32_t vo = voff0 + static_cast<uint32_t>(tb * 16 * row_bytes);
 #pragma unroll
     for (int ld = 0; ld < NLD; ++ld)
-      stage[tb][ld] = __builtin_amdgcn_raw_buffer_load_b128(rc, vo + ld * Tr::byte_offset(32 * KPL), 0, 0);
+      stage[bf][tb][ld] = __builtin_amdgcn_raw_buffer_load_b128(rc, vo + ld * Tr::byte_offset(32 * KPL), 0, 0);
     if constexpr (CT == CT_I8) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.c_scales + row0, (L - t0) * 4);
       const float sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (tb * 16 + li) * 4, 0, 0));
 #pragma unroll
-      for (int ld = 0; ld < NLD; ++ld) sscale[tb][ld] = sc;
+      for (int ld = 0; ld < NLD; ++ld) sscale[bf][tb][ld] = sc;
     }
     if constexpr (CT == CT_I4) {
       const int groups = r / 128;
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.c_scales + row0 * groups, (L - t0) * groups * 4);
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld)
-        sscale[tb][ld] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        sscale[bf][tb][ld] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             rs, ((tb * 16 + li) * groups + (j0w + 128 * ld) / 128) * 4, 0, 0));
     }
   };
+  auto tile_start = [&](int it) { return (static_cast<int64_t>(split) + static_cast<int64_t>(it) * p.S) * T; };
 
-  if (ntiles > 0) {
+  // the first D tiles are requested before anything else
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) load_rows(static_cast<int64_t>(split) * T, tb);
+  for (int tb = 0; tb < NTB; ++tb)
+    if (ntiles > 0) load_rows(std::integral_constant<int, 0>{}, tile_start(0), tb);
+  if constexpr (D == 2) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+      if (ntiles > 1) load_rows(std::integral_constant<int, D - 1>{}, tile_start(1), tb);
   }
 
   // Absorbed queries as the B operand of the score product.  K block
@@ -465,6 +476,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       qf[hb][kb] = __builtin_bit_cast(bf16x8, v);
     }
 
+  // O~ transposed: oacc[hb][jb] holds columns 16 jb + 4 g + (0..3) of head 16 hb + i
   f32x4 oacc[NHB][NJB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
@@ -475,46 +487,46 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
     m_s[i] = -INFINITY;
     l_s[i] = 0.f;
   }
-
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int64_t tile_t0 = (static_cast<int64_t>(split) + static_cast<int64_t>(it) * p.S) * T;
-    const bool more = it + 1 < ntiles;
-    const int64_t next_t0 = tile_t0 + static_cast<int64_t>(p.S) * T;
+  auto body = [&](auto BUF, int it) {
+    constexpr int bf = decltype(BUF)::value;
+    const int64_t tile_t0 = tile_start(it);
+    const bool more = it + D < ntiles;
+    const int64_t next_t0 = tile_start(it + D);
 
     // ---- 1-3. per 16-token row block: bf16 A operands, partial scores over
-    // this wavefront's columns, the rows to LDS, then the next tile's loads
+    // this wavefront's columns, the rows to LDS, then the loads D tiles ahead
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       u32x4 cv[NKB];
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
         if constexpr (CT == CT_BF16) {
-          cv[ld] = stage[tb][ld];
+          cv[ld] = stage[bf][tb][ld];
         } else if constexpr (CT == CT_I8) {
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             uint32_t o[4];
 #pragma unroll
             for (int w2 = 0; w2 < 2; ++w2) {
-              const uint32_t word = stage[tb][ld][2 * s + w2];
+              const uint32_t word = stage[bf][tb][ld][2 * s + w2];
               o[2 * w2] = dq_pair(static_cast<int>(word << 24) >> 24,
-                                  static_cast<int>(word << 16) >> 24, sscale[tb][ld]);
+                                  static_cast<int>(word << 16) >> 24, sscale[bf][tb][ld]);
               o[2 * w2 + 1] = dq_pair(static_cast<int>(word << 8) >> 24,
-                                      static_cast<int>(word) >> 24, sscale[tb][ld]);
+                                      static_cast<int>(word) >> 24, sscale[bf][tb][ld]);
             }
             cv[2 * ld + s] = u32x4{o[0], o[1], o[2], o[3]};
           }
         } else {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const uint32_t word = stage[tb][ld][s];
+            const uint32_t word = stage[bf][tb][ld][s];
             uint32_t o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               o[e] = dq_pair(static_cast<int>(word << (28 - 8 * e)) >> 28,
-                             static_cast<int>(word << (24 - 8 * e)) >> 28, sscale[tb][ld]);
+                             static_cast<int>(word << (24 - 8 * e)) >> 28, sscale[bf][tb][ld]);
             cv[4 * ld + s] = u32x4{o[0], o[1], o[2], o[3]};
           }
         }
@@ -534,7 +546,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         const int jl = 32 * KPL * ld + EPL * lg + 8 * s;
         *reinterpret_cast<u32x4 *>(ct + (tb * 16 + li) * RS + jl * 2) = cv[kb];
       }
-      if (more) load_rows(next_t0, tb);
+      if (more) load_rows(BUF, next_t0, tb);
       // partial scores, head-major: lane holds tokens 16 tb + 4 g + (0..3) of head 16 hb + i
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
@@ -569,82 +581,104 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         l_s[h] = fmaf(l_s[h], alpha, psum);
         alpha_s[h] = alpha;
       }
-      // P as the A operand of the value product: lane 16 (t / PPL) + h % 16, element t % PPL
+      // P as the B operand of the value product: lane 16 (t / PPL) + h % 16, element t % PPL
       uint16_t *pdst = pl + ((h >> 4) * 64 + 16 * (t0 / PPL) + (h & 15)) * PPL + (t0 % PPL);
       *reinterpret_cast<uint32_t *>(pdst) = pp;
     }
     __syncthreads();
 
-    // ---- 5. O~ = O~ * alpha + P^T C_tile (the rescale is skipped by a
+    // ---- 5. O~^T = O~^T * alpha + C_tile^T P^T (the rescale is skipped by a
     // wavefront whose heads all kept their running maximum)
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const f32x4 al = *reinterpret_cast<const f32x4 *>(alpha_s + hb * 16 + 4 * lg);
-      const bool keep = al[0] == 1.f && al[1] == 1.f && al[2] == 1.f && al[3] == 1.f;
-      if (__builtin_amdgcn_ballot_w64(!keep) != 0) {
+      const float al = alpha_s[hb * 16 + li];
+      if (__builtin_amdgcn_ballot_w64(al != 1.f) != 0) {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) oacc[hb][jb][e] *= al[e];
+          for (int e = 0; e < 4; ++e) oacc[hb][jb][e] *= al;
       }
     }
-    // B operand: tokens PPL g + (0..PPL-1) of column 16 jb + lane % 16, by
+    // A operand: column 16 jb + lane % 16, tokens PPL g + (0..PPL-1), by
     // transposing 8-byte reads of 4 tokens each (lane i of a 16-lane group
     // supplies row i / 4 and columns 4 (i % 4) .. +3 of a 4 x 16 block).
     const uint8_t *trb = ct + (PPL * lg + (li >> 2)) * RS + (4 * (li & 3)) * 2;
     if constexpr (T == 32) {
-      bf16x8 pa[NHB];
+      bf16x8 pb[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        pa[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(pl + (hb * 64 + lane) * PPL));
+        pb[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(pl + (hb * 64 + lane) * PPL));
+      // column blocks in groups of VB: all transposing reads of a group are
+      // issued before its products
+      constexpr int VB = (NJB % 4 == 0) ? 4 : ((NJB % 3 == 0) ? 3 : 2);
+      static_assert(NJB % VB == 0, "column groups");
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x4 lo = lds_read_tr16(trb + jb * 32);
-        const bf16x4 hi = lds_read_tr16(trb + 4 * RS + jb * 32);
-        const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int jg = 0; jg < NJB; jg += VB) {
+        bf16x4 lo[VB], hi[VB];
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb)
-          oacc[hb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[hb], bv, oacc[hb][jb], 0, 0, 0);
+        for (int k = 0; k < VB; ++k) {
+          lo[k] = lds_read_tr16(trb + (jg + k) * 32);
+          hi[k] = lds_read_tr16(trb + 4 * RS + (jg + k) * 32);
+        }
+#pragma unroll
+        for (int k = 0; k < VB; ++k) {
+          const bf16x8 av = __builtin_shufflevector(lo[k], hi[k], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+            oacc[hb][jg + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hb], oacc[hb][jg + k], 0, 0, 0);
+        }
       }
     } else {
-      bf16x4 pa[NHB];
+      bf16x4 pb[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        pa[hb] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(pl + (hb * 64 + lane) * PPL));
+        pb[hb] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(pl + (hb * 64 + lane) * PPL));
+      constexpr int VB = (NJB % 4 == 0) ? 4 : ((NJB % 3 == 0) ? 3 : 2);
+      static_assert(NJB % VB == 0, "column groups");
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x4 bv = lds_read_tr16(trb + jb * 32);
+      for (int jg = 0; jg < NJB; jg += VB) {
+        bf16x4 av[VB];
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb)
-          oacc[hb][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[hb], bv, oacc[hb][jb], 0, 0, 0);
+        for (int k = 0; k < VB; ++k) av[k] = lds_read_tr16(trb + (jg + k) * 32);
+#pragma unroll
+        for (int k = 0; k < VB; ++k)
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+            oacc[hb][jg + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[k], pb[hb], oacc[hb][jg + k], 0, 0, 0);
       }
+    }
+  };
+
+  for (int it = 0; it < ntiles; it += D) {
+    body(std::integral_constant<int, 0>{}, it);
+    if constexpr (D == 2) {
+      if (it + 1 < ntiles) body(std::integral_constant<int, 1>{}, it + 1);
     }
   }
   __syncthreads();
 
-  // ---- partial state: O~ / l (bf16, [head][RW] rows staged in this
-  // wavefront's LDS tile, then 16-byte stores) and (m, l)
+  // ---- partial state: O~ / l in bf16, one contiguous block per wavefront
+  // ([sequence][split][wavefront][head][RW]), staged in the wavefront's LDS
+  // tile so that the stores are 16-byte and contiguous; and (m, l)
   const int64_t pbase = (static_cast<int64_t>(seq) * p.S + split) * p.heads + h0;
   {
-    uint16_t *ot = reinterpret_cast<uint16_t *>(ct);  // [HGP][RW]; HGP * RW * 2 <= T * RS
+    uint16_t *ot = reinterpret_cast<uint16_t *>(ct);  // [HGP][RW]
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int h = hb * 16 + li;
+      const float l = l_s[h];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int h = hb * 16 + 4 * lg + e;
-        const float l = l_s[h];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) ot[h * RW + jb * 16 + li] = f32_to_bf16(oacc[hb][jb][e] * inv);
-      }
-    // same-wavefront LDS write -> read: ordered by the LDS queue
-    constexpr int UPR = RW / 8;  // 16-byte units per head row
-    for (int u = lane; u < HGP * UPR; u += 64) {
-      const int h = u / UPR, c8 = (u % UPR) * 8;
-      if (h < hg)
-        *reinterpret_cast<u32x4 *>(p.opart + (pbase + h) * r + j0w + c8) =
-            *reinterpret_cast<const u32x4 *>(ot + h * RW + c8);
+      for (int jb = 0; jb < NJB; ++jb)
+        *reinterpret_cast<u32x2 *>(ot + h * RW + jb * 16 + 4 * lg) =
+            u32x2{cvt_bf16x2(oacc[hb][jb][0] * inv, oacc[hb][jb][1] * inv),
+                  cvt_bf16x2(oacc[hb][jb][2] * inv, oacc[hb][jb][3] * inv)};
     }
+    // same-wavefront LDS write -> read, ordered by the LDS queue
+    uint16_t *dst = p.opart + ((static_cast<int64_t>(seq) * p.S + split) * W + wave) *
+                                  static_cast<int64_t>(p.heads) * RW + static_cast<int64_t>(h0) * RW;
+    for (int u = lane; u < hg * RW / 8; u += 64)
+      *reinterpret_cast<u32x4 *>(dst + u * 8) = *reinterpret_cast<const u32x4 *>(ot + u * 8);
   }
   for (int h = tid; h < hg; h += nthreads) {
     p.ml[2 * (pbase + h)] = m_s[h];
@@ -653,28 +687,30 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 }
 
 // ------------------------------------------------------------------ MFMA merge
-// Workgroup (chunk jc of kMergeRows latent rows, head h, 16 sequences):
-//   1. the chunk of W^u_v,h (kMergeRows x d) is fetched into registers (int8
-//      codes are exact in bf16; their column scales multiply the result);
-//   2. log-sum-exp weights of every split (16 lanes per sequence);
-//   3. merged O~ rows of the chunk (8 rows per thread, the partial loads of 8
-//      splits in flight at once), written to LDS as the A operand of
-//      v_mfma_f32_16x16x32_bf16 (M = 16 sequences, K = latent rows);
-//   4. O~ W^u_v,h with the B operand read by transposing LDS loads ->
-//      opj[jc][b][h][:] (float32).
-// W^u_v is read once per (chunk, head, 16 sequences).  A device-scope fence
-// per workgroup to let the last chunk sum the shares costs more than a
-// separate finalize launch (the release writes back the L2), so the shares
-// are summed by decode_finalize.
+// Workgroup (chunk jc of kMergeRows latent rows, head h, 16 sequences).  All
+// global loads are issued up front (one memory round trip):
+//   - the chunk of W^u_v,h (kMergeRows x d) into registers (int8 codes are
+//     exact in bf16; their column scales multiply the result);
+//   - (m, l) of every split (thread = sequence tid / 16, splits tid % 16 + 16 k);
+//   - the partial O~ rows of up to kMergeBatch splits (thread = sequence
+//     tid / 16, rows 8 (tid % 16) .. +8).
+// Then: log-sum-exp weights (16-lane DPP reductions), the merged O~ rows as
+// the A operand of v_mfma_f32_16x16x32_bf16 (M = 16 sequences, K = latent
+// rows) in LDS, the W chunk to LDS, and O~ W^u_v,h with the B operand read by
+// transposing LDS loads -> opj[jc][b][h][:] (float32), summed over the chunks
+// by decode_finalize.  W^u_v is read once per (chunk, head, 16 sequences).
+constexpr int kMergeBatch = 16;
+
 template <typename WT>
 __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restrict__ opart,
                                                          const float *__restrict__ ml,
                                                          const WT *__restrict__ Wv,
                                                          const float *__restrict__ wscale,
                                                          float *__restrict__ opj, int b, int r,
-                                                         int heads, int d, int S) {
+                                                         int heads, int d, int S, int RW) {
   constexpr int BB = 16;
   constexpr int MAXU = kMergeRows * 256 / 8 / 256;  // 8-column W units per thread (d <= 256)
+  constexpr int MAXSL = 4;                          // splits per thread held in registers (S <= 64)
   extern __shared__ __attribute__((aligned(16))) uint8_t msm[];
   const int WRS = d * 2 + 16;                                       // W chunk row stride (bytes)
   uint8_t *wl = msm;                                                // [kMergeRows][WRS]
@@ -687,8 +723,11 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
   const int rows = min(kMergeRows, r - j0);  // multiple of 32
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int units = d / 8;                   // 8-column units per row
+  const int bi = tid >> 4, sl = tid & 15, jj0 = sl * 8;
+  const int bseq = b0 + min(bi, nbb - 1);
+  const bool rvalid = bi < nbb && jj0 < rows;
 
-  // 1. W^u_v chunk -> registers
+  // ---- all loads
   u32x4 wreg[MAXU];
 #pragma unroll
   for (int k = 0; k < MAXU; ++k) {
@@ -705,27 +744,55 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
       }
     }
   }
+  const int64_t mlbase = static_cast<int64_t>(bseq) * S * heads + h;
+  float2 mlv[MAXSL];
+#pragma unroll
+  for (int k = 0; k < MAXSL; ++k) {
+    const int s = sl + 16 * k;
+    mlv[k] = (s < S) ? *reinterpret_cast<const float2 *>(ml + 2 * (mlbase + static_cast<int64_t>(s) * heads))
+                     : float2{-INFINITY, 0.f};
+  }
+  // partial rows of (sequence, split, head): wavefront-blocked layout
+  // [sequence][split][r / RW][head][RW]; consecutive splits are heads * r apart
+  const int jrow = j0 + min(jj0, rows - 8);
+  const uint16_t *psrc = opart + (static_cast<int64_t>(bseq) * S * (r / RW) + jrow / RW) * heads * RW +
+                         static_cast<int64_t>(h) * RW + jrow % RW;
+  const int64_t sstride = static_cast<int64_t>(heads) * r;
+  u32x4 pv[kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    pv[k] = u32x4{0u, 0u, 0u, 0u};
+    if (rvalid && k < S) pv[k] = *reinterpret_cast<const u32x4 *>(psrc + k * sstride);
+  }
 
-  // 2. split weights: thread (sequence tid / 16, splits tid % 16, +16, ...)
+  // ---- split weights: w_s = 2^(m_s - M) l_s / sum
   {
-    const int bi = tid >> 4, sl = tid & 15;
-    const int64_t base = static_cast<int64_t>(b0 + min(bi, nbb - 1)) * S * heads + h;
     float mx = -INFINITY;
-    for (int s = sl; s < S; s += 16) mx = fmaxf(mx, ml[2 * (base + static_cast<int64_t>(s) * heads)]);
-    mx = group_max<16>(mx);
+#pragma unroll
+    for (int k = 0; k < MAXSL; ++k) mx = fmaxf(mx, mlv[k].x);
+    for (int s = sl + 16 * MAXSL; s < S; s += 16)
+      mx = fmaxf(mx, ml[2 * (mlbase + static_cast<int64_t>(s) * heads)]);
+    mx = dpp_reduce<16, true>(mx);
     float den = 0.f;
-    for (int s = sl; s < S; s += 16) {
-      const int64_t o = base + static_cast<int64_t>(s) * heads;
-      const float w = (mx == -INFINITY) ? 0.f : exp2f(ml[2 * o] - mx) * ml[2 * o + 1];
+#pragma unroll
+    for (int k = 0; k < MAXSL; ++k) {
+      const int s = sl + 16 * k;
+      const float w = (mx == -INFINITY || s >= S) ? 0.f : __builtin_amdgcn_exp2f(mlv[k].x - mx) * mlv[k].y;
+      if (s < S) wts[bi * S + s] = w;
+      den += w;
+    }
+    for (int s = sl + 16 * MAXSL; s < S; s += 16) {
+      const int64_t o = mlbase + static_cast<int64_t>(s) * heads;
+      const float w = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[2 * o] - mx) * ml[2 * o + 1];
       wts[bi * S + s] = w;
       den += w;
     }
-    den = group_sum<16>(den);
+    den = dpp_reduce<16, false>(den);
     const float inv = den > 0.f ? 1.f / den : 0.f;
     for (int s = sl; s < S; s += 16) wts[bi * S + s] *= inv;
   }
 
-  // W registers -> LDS (bf16)
+  // ---- W registers -> LDS (bf16)
 #pragma unroll
   for (int k = 0; k < MAXU; ++k) {
     const int u = tid + 256 * k;
@@ -737,8 +804,8 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
         for (int e = 3; e >= 0; --e) {
           const uint32_t word = v[e >> 1];
           const int sh = 16 * (e & 1);
-          v[e] = pack_bf16x2(static_cast<float>(static_cast<int>(word << (24 - sh)) >> 24),
-                             static_cast<float>(static_cast<int>(word << (16 - sh)) >> 24));
+          v[e] = cvt_bf16x2(static_cast<float>(static_cast<int>(word << (24 - sh)) >> 24),
+                            static_cast<float>(static_cast<int>(word << (16 - sh)) >> 24));
         }
       }
       *reinterpret_cast<u32x4 *>(wl + row * WRS + c8 * 2) = v;
@@ -746,39 +813,46 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
   }
   __syncthreads();
 
-  // 3. merged O~ rows: thread (sequence tid / 16, rows 8 (tid % 16) .. +8)
+  // ---- merged O~ rows
   {
-    const int bi = tid >> 4, jj0 = (tid & 15) * 8;
-    const bool valid = bi < nbb && jj0 < rows;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const int64_t base = static_cast<int64_t>(b0 + min(bi, nbb - 1)) * S * heads + h;
-    const uint16_t *src = opart + base * r + j0 + min(jj0, rows - 8);
-    const int64_t sstride = static_cast<int64_t>(heads) * r;
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      u32x4 v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        v[k] = u32x4{0u, 0u, 0u, 0u};
-        if (valid && s0 + k < S) v[k] = *reinterpret_cast<const u32x4 *>(src + (s0 + k) * sstride);
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float w = (k < S) ? wts[bi * S + k] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(w, __uint_as_float(pv[k][e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(w, __uint_as_float(pv[k][e] & 0xFFFF0000u), acc[2 * e + 1]);
+      }
+    }
+    for (int s0 = kMergeBatch; s0 < S; s0 += kMergeBatch) {
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        pv[k] = u32x4{0u, 0u, 0u, 0u};
+        if (rvalid && s0 + k < S) pv[k] = *reinterpret_cast<const u32x4 *>(psrc + (s0 + k) * sstride);
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < kMergeBatch; ++k) {
         const float w = (s0 + k < S) ? wts[bi * S + s0 + k] : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(w, __uint_as_float(v[k][e] << 16), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(w, __uint_as_float(v[k][e] & 0xFFFF0000u), acc[2 * e + 1]);
+          acc[2 * e] = fmaf(w, __uint_as_float(pv[k][e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w, __uint_as_float(pv[k][e] & 0xFFFF0000u), acc[2 * e + 1]);
         }
       }
     }
+    if (!rvalid) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    }
     // A operand of K block jj0 / 32: lane 16 ((jj0 / 8) % 4) + sequence
     aop[(jj0 >> 5) * 64 + 16 * ((jj0 >> 3) & 3) + bi] =
-        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+        u32x4{cvt_bf16x2(acc[0], acc[1]), cvt_bf16x2(acc[2], acc[3]),
+              cvt_bf16x2(acc[4], acc[5]), cvt_bf16x2(acc[6], acc[7])};
   }
   __syncthreads();
 
-  // 4. O~ W^u_v,h: wavefront w takes 16-column blocks w, w + 4, ...
+  // ---- O~ W^u_v,h: wavefront w takes 16-column blocks w, w + 4, ...
   const int li = lane & 15, lg = lane >> 4;
   const int nkb = rows / 32;
   for (int nb = wave; nb < d / 16; nb += 4) {
@@ -795,11 +869,10 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
     const float sc = wscale ? wscale[static_cast<int64_t>(h) * d + col] : 1.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int bi = 4 * lg + e;
-      if (bi < nbb) opj[((static_cast<int64_t>(jc) * b + b0 + bi) * heads + h) * d + col] = acc[e] * sc;
+      const int bo = 4 * lg + e;
+      if (bo < nbb) opj[((static_cast<int64_t>(jc) * b + b0 + bo) * heads + h) * d + col] = acc[e] * sc;
     }
   }
-
 }
 
 // ------------------------------------------------------------------ merge
@@ -960,9 +1033,9 @@ constexpr size_t kMaxLds = 160 * 1024;
 // K blocks per 16-byte cache load for a cache dtype.
 int kpl_of(int c_dtype) { return c_dtype == QSVD_I4 ? 4 : (c_dtype == QSVD_I8 ? 2 : 1); }
 
-template <int CT, int NHB, int NKB, int T>
+template <int CT, int NHB, int NKB, int T, int D>
 hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
-  auto kern = stream_mfma_kernel<CT, NHB, NKB, T>;
+  auto kern = stream_mfma_kernel<CT, NHB, NKB, T, D>;
   const size_t lds = stream_lds_bytes(W, NHB, NKB, T);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -975,10 +1048,10 @@ hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
 template <int CT, int NHB, int NKB>
 hipError_t launch_stream_tile(const StreamParams &sp, const MfmaShape &sh, hipStream_t s) {
   if constexpr (NHB == 2) {
-    return launch_stream_t<CT, NHB, NKB, 32>(sp, sh.W, s);  // mfma_shape pairs NHB = 2 with T = 32
+    return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);  // mfma_shape pairs NHB = 2 with T = 32
   } else {
-    if (sh.T == 32) return launch_stream_t<CT, NHB, NKB, 32>(sp, sh.W, s);
-    return launch_stream_t<CT, NHB, NKB, 16>(sp, sh.W, s);
+    if (sh.T == 32) return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);
+    return launch_stream_t<CT, NHB, NKB, 16, 2>(sp, sh.W, s);
   }
 }
 
@@ -1093,7 +1166,7 @@ hipError_t launch_merge_mfma(const DecodeArgs &a, const DecodePlan &p, const uin
   if (e != hipSuccess) return e;
   kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
       opart, ml, static_cast<const WT *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
-      p.splits);
+      p.splits, a.r / p.shape.W);
   return hipGetLastError();
 }
 
@@ -1137,6 +1210,13 @@ bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
     s.NKB = nkb;
     s.NHB = (heads > 16 && nkb <= 6 && stream_lds_bytes(W, 2, nkb, 32) <= kMaxLds) ? 2 : 1;
     s.T = (nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32) <= kMaxLds) ? 32 : 16;
+    // tuning override of the tile (32: one tile of loads in flight, 16: two)
+    static const int tile_env = [] {
+      const char *e = std::getenv("QSVD_STREAM_TILE");
+      return e ? std::atoi(e) : 0;
+    }();
+    if (tile_env == 16 && s.NHB == 1) s.T = 16;
+    if (tile_env == 32 && nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32) <= kMaxLds) s.T = 32;
     if (stream_lds_bytes(W, s.NHB, nkb, s.T) > kMaxLds) return false;
     if (out) *out = s;
     return true;
