@@ -41,7 +41,7 @@ __all__ = [
     "Config", "CONFIGS", "rng", "haar_columns", "spectrum", "outlier_channels",
     "activations", "Layer", "make_layer", "block_hadamard", "to_bf16_bits",
     "bf16_bits_to_f64", "int8_columns", "decode_case", "DecodeCase",
-    "c4_ranks", "c4_layer", "sharpen_query",
+    "c4_ranks", "c4_layer", "sharpen_query", "quant_decode_inputs", "QuantDecodeInputs",
 ]
 
 
@@ -357,3 +357,39 @@ def prefill_activations(M: int, E: int, frac: float = 0.01, gain: float = 50.0, 
     """Prefill input rows X [M][E] (float64) with the outlier channels of the 7B shape."""
     ch = outlier_channels(E, frac, rng(seed, _OUTLIER))
     return activations(M, E, ch, gain, rng(seed, _X, 0))
+
+
+@dataclasses.dataclass
+class QuantDecodeInputs:
+    """Raw inputs of a W8A4 decode step (config 2): the activations of each
+    sequence, the stored int8 weights and the bf16 query.  The quantisation
+    chain that turns X into the cached int4 latent (rotate + int8, projection,
+    rotate + int4) is a step of the hot path and is not performed here."""
+    E: int
+    heads: int
+    d: int
+    r: int
+    L: int
+    X: list                 # per sequence [L][E] float64 (cached tokens)
+    q: np.ndarray           # [b][heads][d] bf16 bits
+    weights: dict           # quantised_layer_inputs(...)
+    softmax_scale: float
+
+
+def quant_decode_inputs(cfg: Config, seqs, L: int | None = None) -> QuantDecodeInputs:
+    """Inputs of the W8A4 decode step for the listed sequences (same values as in
+    the full batch).  W^d' = H1 W^d is int8 per column (its column scales carry
+    Sigma^beta), W^u' = H2 W^u int8 per column; the query is q = (x_new W^d) W^u_q."""
+    L = cfg.L if L is None else L
+    seed = 1000 + cfg.idx
+    beta = config_beta(cfg)
+    w = quantised_layer_inputs(cfg.E, cfg.r, cfg.p, beta, cfg.hadamard, (seed, 0))
+    layer = w["layer"]
+    channels = outlier_channels(cfg.E, cfg.outlier_frac, rng(seed, _OUTLIER))
+    Xs, qs = [], []
+    for s in seqs:
+        X = activations(L + 1, cfg.E, channels, cfg.outlier_gain, rng(seed, _X, s))
+        Xs.append(X[:L])
+        qs.append(((X[L] @ layer.Wd) @ layer.Wu_q).reshape(cfg.heads, cfg.d))
+    return QuantDecodeInputs(cfg.E, cfg.heads, cfg.d, cfg.r, L, Xs, to_bf16_bits(np.stack(qs)), w,
+                             1.0 / math.sqrt(cfg.d))
