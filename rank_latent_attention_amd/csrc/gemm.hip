@@ -6,145 +6,239 @@
 // product is an int8 x int8 contraction with per-token and per-column scales.
 //
 // C[M][N] = A[M][K] * B[K][N] with B stored transposed (Bt[N][K]) so both
-// operands are contiguous along K, the layout MFMA operands want.  One
-// workgroup (4 wavefronts) computes a 128 x 128 tile; each wavefront owns
-// 64 x 64 = 2 x 2 MFMA 32x32 blocks.  A K-step is 64 bytes of each operand row
-// (64 int8 or 32 bf16), staged through double-buffered LDS.
+// operands are contiguous along K, the layout MFMA operands want.
 //   int8: v_mfma_i32_32x32x32_i8, exact int32 accumulation; epilogue
 //         float32(float32(float32(acc) * a_scale[m]) * col_scale[n]).
 //   bf16: v_mfma_f32_32x32x16_bf16, float32 accumulation; * col_scale[n].
-// The blockIdx -> tile map keeps the row blocks of one XCD contiguous so an
-// A tile is fetched into a single XCD's L2.
+//
+// Data path.  A workgroup computes a BM x BN tile with WM x WN wavefronts
+// (two per SIMD), each owning (BM/WM) x (BN/WN) in 32 x 32 MFMA blocks.  A K
+// stage is 128 bytes of every operand row (one cache line), moved from global
+// memory straight into LDS by buffer_load ... lds (no VGPR staging, no LDS
+// store instructions); two LDS slots, the next stage in flight while the
+// current one is multiplied.  In LDS, the 16-byte chunk c of row r sits at
+// position c ^ g(r) of its 128-byte row, which makes the MFMA operand reads
+// (32 consecutive rows, one chunk) free of bank conflicts.  The epilogue
+// transposes each 32 x 32 block through LDS so that every lane writes four
+// consecutive outputs of a row.  The blockIdx -> tile map keeps the row
+// blocks of one XCD contiguous so an A tile is fetched into a single XCD's L2.
 #include "device_common.h"
 #include "qsvd_internal.h"
+
+#include <climits>
+#include <cstdint>
+#include <type_traits>
 
 namespace qsvd {
 namespace {
 
-constexpr int BM = 128, BN = 128, BKB = 64;  // tile rows, cols, K bytes per step
-constexpr int LDS_STRIDE = BKB + 16;         // padded row stride in LDS (bytes)
+constexpr int kComputeUnits = 256;       // gfx950: 8 XCDs x 32 CUs
+constexpr int BK = 128;                  // K bytes per stage (128 int8 or 64 bf16)
+constexpr int kRowsPerDma = 1024 / BK;   // one buffer_load ... lds moves 64 x 16 bytes
+constexpr int kEpiStride = 36;           // epilogue block row stride (32-bit words)
 
-template <bool INT8, bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ A,
-                                                   const float *__restrict__ a_scale, int64_t M,
-                                                   int K, const uint8_t *__restrict__ Bt,
-                                                   const float *__restrict__ col_scale, int N,
-                                                   void *__restrict__ Cout) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][BM * LDS_STRIDE];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_rows(const uint8_t *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), static_cast<short>(0),
+                                           static_cast<int>(n), 0x00020000);
+}
 
-  const int esize = INT8 ? 1 : 2;
-  const int64_t kbytes = static_cast<int64_t>(K) * esize;
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(uint8_t *p) {
+  return (__attribute__((address_space(3))) void *)(p);
+}
+
+// s_waitcnt vmcnt(0) lgkmcnt(0): every DMA of this wavefront has landed in
+// LDS and its LDS reads have returned.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+// position of 16-byte chunk c of LDS row r is c ^ swz(r): distinct for any 8
+// consecutive rows (128-byte bank window) and, with the row parity, for any 16
+// consecutive rows (256-byte window)
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <bool INT8, bool OUT_BF16, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
+                 const uint8_t *__restrict__ Bt, const float *__restrict__ col_scale, int N,
+                 void *__restrict__ Cout) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;            // wavefront tile
+  constexpr int MB = TM / 32, NB = TN / 32;
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wavefront tile");
+  constexpr int SLOT = (BM + BN) * BK;
+  constexpr int BLK_A = BM / kRowsPerDma;
+  constexpr int BLK = (BM + BN) / kRowsPerDma;
+  static_assert(BLK % NW == 0, "DMA blocks split evenly over the wavefronts");
+  constexpr int LPW = BLK / NW;                        // DMA instructions per wavefront per stage
+  static_assert(1024 + NW * 32 * kEpiStride * 4 <= 2 * SLOT, "epilogue fits in the slots");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+
+  const int64_t kbytes = static_cast<int64_t>(K) * (INT8 ? 1 : 2);
   const int nbn = (N + BN - 1) / BN;
-
-  // XCD-aware tile order: workgroup id i runs on XCD i % 8.
-  const int total = gridDim.x;
-  const int id = blockIdx.x;
+  const int total = gridDim.x, id = blockIdx.x;
   const int per = total / 8, rem = total % 8;
   const int xcd = id % 8, local = id / 8;
   const int tile = xcd * per + min(xcd, rem) + local;
   const int64_t m0 = static_cast<int64_t>(tile / nbn) * BM;
   const int n0 = (tile % nbn) * BN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
 
-  // global -> register staging: thread t moves rows t/4 and t/4 + 64, 16-byte chunk t%4
-  const int lrow = tid >> 2, lchunk = (tid & 3) * 16;
-  u32x4 ra[2], rb[2];
-  auto gload = [&](int64_t kb0) {
+  // rows past M (N) read as zero through the buffer range check
+  const __amdgpu_buffer_rsrc_t ra = rsrc_rows(A + m0 * kbytes, (M - m0) * kbytes);
+  const __amdgpu_buffer_rsrc_t rb = rsrc_rows(Bt + static_cast<int64_t>(n0) * kbytes,
+                                              (static_cast<int64_t>(N) - n0) * kbytes);
+  // A DMA instruction fills 8 LDS rows; lane l writes 16 bytes at l * 16, i.e.
+  // row l / 8, position l % 8, so it fetches chunk (l % 8) ^ swz(row).  The
+  // rows of this wavefront's blocks are wave * 8 + l / 8 modulo 16.
+  const int lr = lane >> 3;
+  const uint32_t lane_off =
+      static_cast<uint32_t>(lr * kbytes + (((lane & 7) ^ swz(wave * kRowsPerDma + lr)) * 16));
+
+  // epilogue operands fetched up front
+  float my_as = 0.f;
+  if constexpr (INT8) {
+    if (tid < BM && m0 + tid < M) my_as = a_scale[m0 + tid];
+  }
+  float csr[NB][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t m = m0 + lrow + h * 64;
-      const int n = n0 + lrow + h * 64;
-      ra[h] = (m < M) ? *reinterpret_cast<const u32x4 *>(A + m * kbytes + kb0 + lchunk)
-                      : u32x4{0u, 0u, 0u, 0u};
-      rb[h] = (n < N) ? *reinterpret_cast<const u32x4 *>(Bt + static_cast<int64_t>(n) * kbytes +
-                                                          kb0 + lchunk)
-                      : u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int n = n0 + wn * TN + j * 32 + (lane & 7) * 4 + c;
+      csr[j][c] = (col_scale && n < N) ? col_scale[n] : 1.f;
     }
-  };
-  auto lstore = [&](int buf) {
+
+  auto issue = [&](int stage, int slot) {
+    const uint32_t kb = static_cast<uint32_t>(stage) * BK;
+    uint8_t *base = lds + slot * SLOT;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<u32x4 *>(&lds[buf][0][(lrow + h * 64) * LDS_STRIDE + lchunk]) = ra[h];
-      *reinterpret_cast<u32x4 *>(&lds[buf][1][(lrow + h * 64) * LDS_STRIDE + lchunk]) = rb[h];
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wave + NW * i;
+      if (blk < BLK_A) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, lds_ptr(base + blk * 1024), 16,
+            lane_off + static_cast<uint32_t>(blk * kRowsPerDma * kbytes) + kb, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, lds_ptr(base + blk * 1024), 16,
+            lane_off + static_cast<uint32_t>((blk - BLK_A) * kRowsPerDma * kbytes) + kb, 0, 0, 0);
+      }
     }
   };
 
   using Acc = typename std::conditional<INT8, i32x16, f32x16>::type;
-  Acc acc[2][2];
+  Acc acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  const int nk = static_cast<int>(kbytes / BKB);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(static_cast<int64_t>(kt + 1) * BKB);
+  // operand fragments: row (lane & 31) of a 32-row block, chunk 2 * ks + lane / 32
+  const int fr = lane & 31;
+  const int fsw = swz(fr);
+  auto compute = [&](int slot, int ksteps) {
+    const uint8_t *base = lds + slot * SLOT;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {  // two 32-byte MFMA K-steps per 64-byte stage
-      const int koff = ks * 32 + (lane >> 5) * 16;
-      u32x4 af[2], bf[2];
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      if (ks >= ksteps) break;
+      const int pos = ((ks * 2 + (lane >> 5)) ^ fsw) * 16;
+      u32x4 af[MB], bfr[NB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const u32x4 *>(
-            &lds[buf][0][(wm * 64 + i * 32 + (lane & 31)) * LDS_STRIDE + koff]);
-        bf[i] = *reinterpret_cast<const u32x4 *>(
-            &lds[buf][1][(wn * 64 + i * 32 + (lane & 31)) * LDS_STRIDE + koff]);
-      }
+      for (int i = 0; i < MB; ++i)
+        af[i] = *reinterpret_cast<const u32x4 *>(base + (wm * TM + i * 32 + fr) * BK + pos);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < NB; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4 *>(base + (BM + wn * TN + j * 32 + fr) * BK + pos);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if constexpr (INT8) {
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if constexpr (INT8)
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                __builtin_bit_cast(i32x4, af[i]), __builtin_bit_cast(i32x4, bf[j]), acc[i][j], 0,
-                0, 0);
-          } else {
+                __builtin_bit_cast(i32x4, af[i]), __builtin_bit_cast(i32x4, bfr[j]), acc[i][j], 0, 0, 0);
+          else
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bf[j]), acc[i][j],
-                0, 0, 0);
-          }
+                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
         }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // Epilogue.  32x32 accumulator layout: element e of lane l is
-  // row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+  // K is a multiple of 64 bytes; a last stage of 64 bytes runs two K steps
+  // (its upper half holds the next row's bytes and is not used)
+  const int nk = static_cast<int>((kbytes + BK - 1) / BK);
+  const int last_steps = (kbytes % BK == 0) ? BK / 32 : static_cast<int>(kbytes % BK) / 32;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed for every wavefront and everyone is done reading
+    // the other slot, which then takes stage kt + 1 (past the end, a repeat of
+    // the last stage into a slot that is not read again)
+    wait_all_loads();
+    __builtin_amdgcn_s_barrier();
+    issue(min(kt + 1, nk - 1), (kt + 1) & 1);
+    compute(kt & 1, kt == nk - 1 ? last_steps : BK / 32);
+  }
+  wait_all_loads();
+  __builtin_amdgcn_s_barrier();
+
+  // Epilogue: row scales to LDS; each wavefront writes a 32 x 32 accumulator
+  // block into its own LDS area (element e of lane l is row 8*(e/4) +
+  // 4*(l/32) + e%4, column l%32) and reads it back as 4 consecutive columns
+  // of one row per lane.
+  float *las = reinterpret_cast<float *>(lds);
+  if constexpr (INT8) {
+    if (tid < BM) las[tid] = my_as;
+  }
+  __syncthreads();
+  uint32_t *blk = reinterpret_cast<uint32_t *>(lds + 1024 + wave * (32 * kEpiStride * 4));
+  const int rr = lane >> 3, cc = (lane & 7) * 4;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (n >= N) continue;
-      const float cs = col_scale ? col_scale[n] : 1.f;
+    for (int j = 0; j < NB; ++j) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m >= M) continue;
-        float v;
-        if constexpr (INT8) {
-          v = static_cast<float>(acc[i][j][e]);
-          v = v * a_scale[m];
-          v = v * cs;
-        } else {
-          v = acc[i][j][e] * cs;
-        }
-        if constexpr (OUT_BF16)
-          static_cast<uint16_t *>(Cout)[m * N + n] = f32_to_bf16(v);
-        else
-          static_cast<float *>(Cout)[m * N + n] = v;
+        // (a bit cast of a vector element would read element 0 with this
+        // compiler; convert through a scalar)
+        uint32_t bits;
+        if constexpr (INT8) bits = static_cast<uint32_t>(static_cast<int>(acc[i][j][e]));
+        else bits = __float_as_uint(static_cast<float>(acc[i][j][e]));
+        blk[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * kEpiStride + (lane & 31)] = bits;
       }
+      __builtin_amdgcn_wave_barrier();
+      const int n = n0 + wn * TN + j * 32 + cc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = q * 8 + rr;
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(blk + r * kEpiStride + cc);
+        const int lrow = wm * TM + i * 32 + r;
+        const int64_t m = m0 + lrow;
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t wc = w[c];
+          if constexpr (INT8) {
+            v[c] = static_cast<float>(static_cast<int>(wc));
+            v[c] = v[c] * las[lrow];
+            v[c] = v[c] * csr[j][c];
+          } else {
+            v[c] = __uint_as_float(wc) * csr[j][c];
+          }
+        }
+        if (m < M && n < N) {
+          if constexpr (OUT_BF16) {
+            u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(Cout) + m * N + n) = o;
+          } else {
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(Cout) + m * N + n) = {v[0], v[1], v[2], v[3]};
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -167,29 +261,61 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in
   }
 }
 
+template <bool INT8, bool OUT_BF16, int BM, int BN, int WM, int WN>
+hipError_t run_gemm(const uint8_t *a, const float *a_scale, int64_t M, int K, const uint8_t *b,
+                    const float *col_scale, int N, void *C, hipStream_t s) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  constexpr size_t lds = static_cast<size_t>(2) * (BM + BN) * BK;
+  auto kern = gemm_kernel<INT8, OUT_BF16, BM, BN, WM, WN>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  kern<<<dim3(static_cast<unsigned>(tiles)), dim3(64 * WM * WN), lds, s>>>(a, a_scale, M, K, b,
+                                                                          col_scale, N, C);
+  return hipGetLastError();
+}
+
+template <bool INT8, bool OUT_BF16>
+hipError_t run_gemm_shape(const uint8_t *a, const float *a_scale, int64_t M, int K,
+                          const uint8_t *b, const float *col_scale, int N, void *C,
+                          hipStream_t s) {
+  // Tile choice: a launch takes ceil(tiles / concurrent) rounds, each about
+  // as long as one tile's area per compute unit; pick the least rounds x area
+  // (x workgroups per CU), the larger tile on ties.  16384 x 1536 -> 256 x 384
+  // (256 tiles, one round); 16384 x 512 -> 128 x 256; 16384 x 8192 -> 256 x 256.
+  struct Cand { int bm, bn, per_cu; };
+  static constexpr Cand cands[] = {{256, 384, 1}, {256, 256, 1}, {128, 256, 1}, {128, 128, 2}};
+  int best = 0;
+  int64_t best_cost = INT64_MAX;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
+    const int64_t slots = static_cast<int64_t>(kComputeUnits) * cands[i].per_cu;
+    const int64_t cost = ((tiles + slots - 1) / slots) * cands[i].bm * cands[i].bn * cands[i].per_cu;
+    if (cost < best_cost) { best_cost = cost; best = i; }
+  }
+  switch (best) {
+    case 0: return run_gemm<INT8, OUT_BF16, 256, 384, 2, 4>(a, a_scale, M, K, b, col_scale, N, C, s);
+    case 1: return run_gemm<INT8, OUT_BF16, 256, 256, 2, 4>(a, a_scale, M, K, b, col_scale, N, C, s);
+    case 2: return run_gemm<INT8, OUT_BF16, 128, 256, 2, 4>(a, a_scale, M, K, b, col_scale, N, C, s);
+    default: return run_gemm<INT8, OUT_BF16, 128, 128, 2, 2>(a, a_scale, M, K, b, col_scale, N, C, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void *A, const float *a_scale, bool int8, int64_t M, int K,
                        const void *Bt, const float *col_scale, int N, void *C, bool c_bf16,
                        hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const dim3 grid(static_cast<unsigned>(tiles)), block(256);
   const auto *a = static_cast<const uint8_t *>(A);
   const auto *b = static_cast<const uint8_t *>(Bt);
   LaunchTimer t(int8 ? "gemm_i8" : "gemm_bf16", s);
   if (int8) {
-    if (c_bf16)
-      gemm_kernel<true, true><<<grid, block, 0, s>>>(a, a_scale, M, K, b, col_scale, N, C);
-    else
-      gemm_kernel<true, false><<<grid, block, 0, s>>>(a, a_scale, M, K, b, col_scale, N, C);
-  } else {
-    if (c_bf16)
-      gemm_kernel<false, true><<<grid, block, 0, s>>>(a, a_scale, M, K, b, col_scale, N, C);
-    else
-      gemm_kernel<false, false><<<grid, block, 0, s>>>(a, a_scale, M, K, b, col_scale, N, C);
+    if (c_bf16) return run_gemm_shape<true, true>(a, a_scale, M, K, b, col_scale, N, C, s);
+    return run_gemm_shape<true, false>(a, a_scale, M, K, b, col_scale, N, C, s);
   }
-  return hipGetLastError();
+  if (c_bf16) return run_gemm_shape<false, true>(a, a_scale, M, K, b, col_scale, N, C, s);
+  return run_gemm_shape<false, false>(a, a_scale, M, K, b, col_scale, N, C, s);
 }
 
 hipError_t launch_transpose(const void *W, int elem_bytes, int rows, int cols, void *out,

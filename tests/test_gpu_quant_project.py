@@ -106,6 +106,7 @@ def run_project_i8(A, sa, W, sw, out_bf16=False):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 16), (33, 128, 48), (257, 4096, 1536), (130, 512, 272),
+                                   (77, 192, 48), (300, 1088, 2048), (1000, 4096, 400),
                                    (512, 2048, 8192)])
 def test_project_int8_bit_exact(M, K, N):
     say(f"case: project int8 M={M} K={K} N={N}")
