@@ -111,21 +111,19 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
       csr[j][c] = (col_scale && n < N) ? col_scale[n] : 1.f;
     }
 
-  auto issue = [&](int stage, int slot) {
+  // DMA instruction i (0 <= i < LPW) of a stage: LDS block wave + NW * i
+  auto issue_one = [&](int i, int stage, int slot) {
     const uint32_t kb = static_cast<uint32_t>(stage) * BK;
     uint8_t *base = lds + slot * SLOT;
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int blk = wave + NW * i;
-      if (blk < BLK_A) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, lds_ptr(base + blk * 1024), 16,
-            lane_off + static_cast<uint32_t>(blk * kRowsPerDma * kbytes) + kb, 0, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, lds_ptr(base + blk * 1024), 16,
-            lane_off + static_cast<uint32_t>((blk - BLK_A) * kRowsPerDma * kbytes) + kb, 0, 0, 0);
-      }
+    const int blk = wave + NW * i;
+    if (blk < BLK_A) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, lds_ptr(base + blk * 1024), 16,
+          lane_off + static_cast<uint32_t>(blk * kRowsPerDma * kbytes) + kb, 0, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, lds_ptr(base + blk * 1024), 16,
+          lane_off + static_cast<uint32_t>((blk - BLK_A) * kRowsPerDma * kbytes) + kb, 0, 0, 0);
     }
   };
 
@@ -141,10 +139,17 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
   // operand fragments: row (lane & 31) of a 32-row block, chunk 2 * ks + lane / 32
   const int fr = lane & 31;
   const int fsw = swz(fr);
-  auto compute = [&](int slot, int ksteps) {
+  // One stage: per 32-byte K step, the operand reads, a share of the next
+  // stage's DMA instructions, then the MFMAs; the scheduling groups interleave
+  // the DMA issue with the MFMAs so neither waits for the other.
+  constexpr int KSTEPS = BK / 32;
+  constexpr int PER = (LPW + KSTEPS - 1) / KSTEPS;     // DMA instructions per K step
+  auto compute = [&](int slot, int ksteps, int nstage, int nslot) {
     const uint8_t *base = lds + slot * SLOT;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      // a short last stage skips its tail steps and the DMA shares issued
+      // there, which only repeat the last stage into a slot that is not read
       if (ks >= ksteps) break;
       const int pos = ((ks * 2 + (lane >> 5)) ^ fsw) * 16;
       u32x4 af[MB], bfr[NB];
@@ -154,6 +159,9 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         bfr[j] = *reinterpret_cast<const u32x4 *>(base + (BM + wn * TN + j * 32 + fr) * BK + pos);
+#pragma unroll
+      for (int q = 0; q < PER; ++q)
+        if (ks * PER + q < LPW) issue_one(ks * PER + q, nstage, nslot);
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -165,6 +173,13 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
         }
+      __builtin_amdgcn_sched_group_barrier(0x100, MB + NB, 0);   // LDS operand reads
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // 1 DMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);   // the remaining MFMAs
     }
   };
 
@@ -172,15 +187,15 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
   // (its upper half holds the next row's bytes and is not used)
   const int nk = static_cast<int>((kbytes + BK - 1) / BK);
   const int last_steps = (kbytes % BK == 0) ? BK / 32 : static_cast<int>(kbytes % BK) / 32;
-  issue(0, 0);
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) issue_one(i, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed for every wavefront and everyone is done reading
-    // the other slot, which then takes stage kt + 1 (past the end, a repeat of
-    // the last stage into a slot that is not read again)
+    // the other slot, which takes stage kt + 1 during this stage's MFMAs (past
+    // the end, a repeat of the last stage into a slot that is not read again)
     wait_all_loads();
     __builtin_amdgcn_s_barrier();
-    issue(min(kt + 1, nk - 1), (kt + 1) & 1);
-    compute(kt & 1, kt == nk - 1 ? last_steps : BK / 32);
+    compute(kt & 1, kt == nk - 1 ? last_steps : BK / 32, min(kt + 1, nk - 1), (kt + 1) & 1);
   }
   wait_all_loads();
   __builtin_amdgcn_s_barrier();
