@@ -19,7 +19,8 @@ Sources (cited by page title and section):
 Conventions (readings of points the pages leave open, listed in the design notes):
 row-vector tokens X in R^{L x E}; Q = X W_Q; W_concat = [W_Q | W_K | W_V];
 W^u split by column blocks in Q, K, V order; head h owns columns
-[h d, (h+1) d); softmax scale 1/sqrt(d), no mask, no positional rotation.
+[h d, (h+1) d); softmax scale 1/sqrt(d), no mask; no positional rotation except
+in attend_explicit_rope (the explicit-reconstruction variant).
 
 Floating point: everything is float64 except the explicitly emulated float32
 rounding points of the encodings (Walsh-Hadamard rotation, absmax quantiser,
@@ -399,6 +400,62 @@ def attend_latent_from_x(X_ctx, x_new, Wd, Wu, heads: int, d: int) -> np.ndarray
     q = (np.asarray(x_new, np.float64) @ Wd) @ Wu[:, :E]
     return attend_explicit(q.reshape(1, heads, d), C[None], Wu[:, E:2 * E], Wu[:, 2 * E:],
                            heads, d, 1.0 / math.sqrt(d))[0]
+
+
+# ----------------------------------------------------------------------------
+# Rotary position embedding (explicit-reconstruction variant)
+# ----------------------------------------------------------------------------
+
+
+def rope_rotate(x, pos, base: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding of vectors x [..][d] at integer positions pos [..].
+
+    [WSVD-digest] "Key Contributions" (and "Method, 3.4"): the fused decode
+    kernel applies RoPE to the keys it reconstructs on chip.  The pages give
+    no convention; the reading taken here is the split-half one of the LLaMA
+    family the evaluated models use: with i = 0 .. d/2 - 1,
+    theta_i = base^(-2 i / d) and angle a = pos * theta_i,
+        x'[i]       = x[i] cos a - x[i + d/2] sin a
+        x'[i + d/2] = x[i + d/2] cos a + x[i] sin a.
+    Pinned by the complex form (x[i] + j x[i+d/2]) e^{j a}, norm
+    preservation, and relative-position invariance of the attention below."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    a = np.asarray(pos, np.float64)[..., None] * theta
+    c, s = np.cos(a), np.sin(a)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def attend_explicit_rope(q, C, Wu_k, Wu_v, heads: int, d: int, softmax_scale: float,
+                         base: float = 10000.0, pos0: int = 0) -> np.ndarray:
+    """attend_explicit with rotary positions: cached latent t of every
+    sequence is the token at position pos0 + t, the decode query is the token
+    at position pos0 + L - 1 (its own latent is the last cached one).  Keys are
+    rebuilt explicitly, K_h = C_b W^u_k,h, then rotated; the query is rotated;
+    V_h = C_b W^u_v,h is not rotated:
+        s_t = softmax_scale * rope(K_h[t], pos0 + t) . rope(q_h, pos0 + L - 1).
+    Returns O [b][heads][d] (float64).  Pinned by pos0 invariance (only
+    position differences enter) and, at L = 1, by attend_explicit."""
+    q = np.asarray(q, np.float64)
+    C = np.asarray(C, np.float64)
+    Wk = np.asarray(Wu_k, np.float64)
+    Wv = np.asarray(Wu_v, np.float64)
+    b, L = q.shape[0], C.shape[1]
+    kpos = pos0 + np.arange(L)
+    out = np.empty((b, heads, d))
+    for s in range(b):
+        K = C[s] @ Wk
+        V = C[s] @ Wv
+        for h in range(heads):
+            cols = slice(h * d, (h + 1) * d)
+            kr = rope_rotate(K[:, cols], kpos, base)
+            qr = rope_rotate(q[s, h], pos0 + L - 1, base)
+            p = _softmax(softmax_scale * (kr @ qr))
+            out[s, h] = p @ V[:, cols]
+    return out
 
 
 def rel_l2(a, b) -> float:

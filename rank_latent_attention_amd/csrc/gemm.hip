@@ -23,6 +23,7 @@
 // consecutive outputs of a row.  The blockIdx -> tile map keeps the row
 // blocks of one XCD contiguous so an A tile is fetched into a single XCD's L2.
 #include "device_common.h"
+#include "dma_pipe.h"
 #include "qsvd_internal.h"
 
 #include <climits>
@@ -32,29 +33,15 @@
 namespace qsvd {
 namespace {
 
+using dma::BK;
+using dma::kRowsPerDma;
+using dma::lds_ptr;
+using dma::rsrc_rows;
+using dma::swz;
+using dma::wait_all_loads;
+
 constexpr int kComputeUnits = 256;       // gfx950: 8 XCDs x 32 CUs
-constexpr int BK = 128;                  // K bytes per stage (128 int8 or 64 bf16)
-constexpr int kRowsPerDma = 1024 / BK;   // one buffer_load ... lds moves 64 x 16 bytes
 constexpr int kEpiStride = 36;           // epilogue block row stride (32-bit words)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_rows(const uint8_t *base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), static_cast<short>(0),
-                                           static_cast<int>(n), 0x00020000);
-}
-
-__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(uint8_t *p) {
-  return (__attribute__((address_space(3))) void *)(p);
-}
-
-// s_waitcnt vmcnt(0) lgkmcnt(0): every DMA of this wavefront has landed in
-// LDS and its LDS reads have returned.
-__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0070); }
-
-// position of 16-byte chunk c of LDS row r is c ^ swz(r): distinct for any 8
-// consecutive rows (128-byte bank window) and, with the row parity, for any 16
-// consecutive rows (256-byte window)
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <bool INT8, bool OUT_BF16, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -93,9 +80,7 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
   // A DMA instruction fills 8 LDS rows; lane l writes 16 bytes at l * 16, i.e.
   // row l / 8, position l % 8, so it fetches chunk (l % 8) ^ swz(row).  The
   // rows of this wavefront's blocks are wave * 8 + l / 8 modulo 16.
-  const int lr = lane >> 3;
-  const uint32_t lane_off =
-      static_cast<uint32_t>(lr * kbytes + (((lane & 7) ^ swz(wave * kRowsPerDma + lr)) * 16));
+  const uint32_t lane_off = dma::lane_offset(lane, wave, kbytes);
 
   // epilogue operands fetched up front
   float my_as = 0.f;

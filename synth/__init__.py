@@ -42,6 +42,7 @@ __all__ = [
     "activations", "Layer", "make_layer", "block_hadamard", "to_bf16_bits",
     "bf16_bits_to_f64", "int8_columns", "decode_case", "DecodeCase",
     "c4_ranks", "c4_layer", "sharpen_query", "quant_decode_inputs", "QuantDecodeInputs",
+    "rope_tables",
 ]
 
 
@@ -393,3 +394,12 @@ def quant_decode_inputs(cfg: Config, seqs, L: int | None = None) -> QuantDecodeI
         qs.append(((X[L] @ layer.Wd) @ layer.Wu_q).reshape(cfg.heads, cfg.d))
     return QuantDecodeInputs(cfg.E, cfg.heads, cfg.d, cfg.r, L, Xs, to_bf16_bits(np.stack(qs)), w,
                              1.0 / math.sqrt(cfg.d))
+
+
+def rope_tables(P: int, d: int, base: float = 10000.0):
+    """Rotary tables a model runtime hands to the explicit decode variant:
+    cos and sin of pos * base^(-2 i / d) for pos < P, i < d/2, as float32
+    [P][d/2] each (computed in float64, rounded once)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    a = np.arange(P, dtype=np.float64)[:, None] * (base ** (-2.0 * i / d))[None, :]
+    return np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)

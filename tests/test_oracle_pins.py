@@ -311,3 +311,39 @@ def test_bf16_round_ties_and_decode():
     assert oracle.bf16_round(np.array([1 + 2 ** -8]))[0] == 1.0
     assert oracle.bf16_round(np.array([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6
     assert oracle.bf16_decode(np.array([0x3F80, 0xBF80], dtype=np.uint16)).tolist() == [1.0, -1.0]
+
+
+# ------------------------------------------------------------------ rotary positions
+def test_rope_matches_complex_rotation_and_preserves_norm():
+    """rope_rotate against the complex form: the pair (x[i], x[i + d/2]) is the
+    complex number x[i] + j x[i + d/2] multiplied by e^{j pos theta_i}."""
+    g = np.random.default_rng(11)
+    d = 16
+    x = g.standard_normal((5, d))
+    pos = np.array([0, 1, 7, 100, 4095])
+    got = oracle.rope_rotate(x, pos, base=500.0)
+    theta = 500.0 ** (-np.arange(d // 2) * 2.0 / d)
+    z = (x[:, : d // 2] + 1j * x[:, d // 2:]) * np.exp(1j * pos[:, None] * theta[None, :])
+    want = np.concatenate([z.real, z.imag], axis=1)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    assert np.allclose(np.linalg.norm(got, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    assert np.array_equal(oracle.rope_rotate(x, np.zeros(5)), x)          # angle 0
+    # two-dimensional case: the plain rotation matrix
+    v = np.array([0.3, -1.7])
+    a = 3.0                                                               # theta_0 = 1
+    R = np.array([[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]])
+    assert np.allclose(oracle.rope_rotate(v, 3), R @ v, atol=1e-15)
+
+
+def test_rope_attention_relative_positions_and_l1():
+    cs = synth.decode_case(256, 2, 128, 96, 2, 40, dtype="f32", seed=9)
+    q, C = cs.q.astype(np.float64), cs.C.astype(np.float64)
+    a = oracle.attend_explicit_rope(q, C, cs.Wu_k, cs.Wu_v, 2, 128, cs.softmax_scale)
+    b = oracle.attend_explicit_rope(q, C, cs.Wu_k, cs.Wu_v, 2, 128, cs.softmax_scale, pos0=777)
+    assert oracle.rel_l2(b, a) < 1e-11                 # only position differences enter
+    plain = oracle.attend_explicit(q, C, cs.Wu_k, cs.Wu_v, 2, 128, cs.softmax_scale)
+    assert oracle.rel_l2(a, plain) > 1e-3              # the rotation does change the result
+    # L = 1: the only key and the query sit at the same position
+    a1 = oracle.attend_explicit_rope(q, C[:, :1], cs.Wu_k, cs.Wu_v, 2, 128, cs.softmax_scale, pos0=5)
+    p1 = oracle.attend_explicit(q, C[:, :1], cs.Wu_k, cs.Wu_v, 2, 128, cs.softmax_scale)
+    assert oracle.rel_l2(a1, p1) < 1e-13
