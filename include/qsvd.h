@@ -163,6 +163,54 @@ qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *
                                float softmax_scale, int32_t splits, void *O, qsvd_dtype_t o_dtype,
                                void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * qsvd_decode_attn_explicit: the same decode step with each head's keys and
+ * values rebuilt explicitly on chip, K_h = C W^u_k,h and V_h = C W^u_v,h,
+ * tile by tile (never written to memory), optionally with rotary position
+ * embedding on the keys and the query.
+ *
+ * Passage: QSVD paper notes, "Key design" (K and V are reconstructed from the
+ * cached latent on demand); WSVD digest, "Method, 3.4" and "Key
+ * Contributions" (a fused flash-decoding pass reconstructs each head's keys
+ * in registers, applies RoPE, and contracts with q without materialising K).
+ * qsvd_decode_attn computes the same attention in the latent space (q folded
+ * into W^u_k) and moves about 16x fewer MFMA operations; this entry point is
+ * the literal reconstruction, and the form that stays valid with RoPE, which
+ * breaks the query folding.
+ *
+ *   q          [b][heads][d] bf16; d must be 128.
+ *   C          [b][L][r] bf16 latent cache; r a multiple of 64.
+ *   Wk_packed, Wv_packed
+ *              W^u_k and W^u_v TRANSPOSED, [E][r] bf16 each (qsvd_pack_weight of
+ *              the [r][E] matrices), E = heads * d.
+ *   rope_cos, rope_sin
+ *              NULL (no rotation) or float32 tables [P][d/2] with P >= L:
+ *              entry [t][i] is cos / sin of t * theta_i.  Cached latent t is
+ *              the token at position t; the query sits at position L - 1 (its
+ *              own latent is the last cached row).  Rotation pairs element i
+ *              with element i + d/2:
+ *                x'[i] = x[i] cos - x[i+d/2] sin,  x'[i+d/2] = x[i+d/2] cos + x[i] sin.
+ *              V is not rotated.
+ *   O          [b][heads][d], o_dtype BF16 or F32.
+ *   workspace  qsvd_decode_explicit_workspace_bytes(b, L, r, heads, d) bytes
+ *              (per (sequence, 256-token tile, head): max, sum and the
+ *              unnormalised 128-wide output, float32).
+ * Errors: QSVD_ERR_UNSUPPORTED for dtypes other than bf16 or d != 128,
+ * QSVD_ERR_INVALID for bad shapes / pointers / a lone RoPE table,
+ * QSVD_ERR_WORKSPACE for a short workspace.  Nothing is launched on error.
+ */
+size_t qsvd_decode_explicit_workspace_bytes(int32_t b, int64_t L, int32_t r, int32_t heads,
+                                            int32_t d);
+
+qsvd_status_t qsvd_decode_attn_explicit(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                        qsvd_dtype_t c_dtype, const void *Wk_packed,
+                                        const void *Wv_packed, qsvd_dtype_t wu_dtype, int32_t b,
+                                        int64_t L, int32_t r, int32_t heads, int32_t d,
+                                        float softmax_scale, const float *rope_cos,
+                                        const float *rope_sin, void *O, qsvd_dtype_t o_dtype,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *hip_stream);
+
 /* The split count qsvd_decode_attn uses when called with splits == 0. */
 int32_t qsvd_decode_default_splits(int32_t b, int64_t L, int32_t r, int32_t heads, int32_t d,
                                    qsvd_dtype_t c_dtype);

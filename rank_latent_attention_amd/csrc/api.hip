@@ -212,6 +212,72 @@ int32_t qsvd_decode_default_splits(int32_t b, int64_t L, int32_t r, int32_t head
   return qsvd::plan_decode(b, L, r, heads, d, c_dtype, 0).splits;
 }
 
+static qsvd_status_t validate_explicit_shape(int32_t b, int64_t L, int32_t r, int32_t heads,
+                                             int32_t d) {
+  if (b < 1) return fail(QSVD_ERR_INVALID, "decode_explicit: b = %d < 1", b);
+  if (L < 1) return fail(QSVD_ERR_INVALID, "decode_explicit: L = %lld < 1", (long long)L);
+  if (heads < 1 || heads > 256) return fail(QSVD_ERR_INVALID, "decode_explicit: heads = %d (1..256)", heads);
+  if (d != 128) return fail(QSVD_ERR_UNSUPPORTED, "decode_explicit: d = %d (128)", d);
+  if (r < 64 || r % 64 != 0 || r > 16384)
+    return fail(QSVD_ERR_INVALID, "decode_explicit: r = %d (a multiple of 64, 64..16384)", r);
+  if (static_cast<int64_t>(b) * L > (int64_t(1) << 36))
+    return fail(QSVD_ERR_INVALID, "decode_explicit: b * L too large");
+  return QSVD_OK;
+}
+
+size_t qsvd_decode_explicit_workspace_bytes(int32_t b, int64_t L, int32_t r, int32_t heads,
+                                            int32_t d) {
+  if (validate_explicit_shape(b, L, r, heads, d) != QSVD_OK) return 0;
+  return qsvd::explicit_workspace_bytes(b, L, heads);
+}
+
+qsvd_status_t qsvd_decode_attn_explicit(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                        qsvd_dtype_t c_dtype, const void *Wk_packed,
+                                        const void *Wv_packed, qsvd_dtype_t wu_dtype, int32_t b,
+                                        int64_t L, int32_t r, int32_t heads, int32_t d,
+                                        float softmax_scale, const float *rope_cos,
+                                        const float *rope_sin, void *O, qsvd_dtype_t o_dtype,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *hip_stream) {
+  qsvd_status_t st = validate_explicit_shape(b, L, r, heads, d);
+  if (st != QSVD_OK) return st;
+  if (q_dtype != QSVD_BF16 || c_dtype != QSVD_BF16 || wu_dtype != QSVD_BF16)
+    return fail(QSVD_ERR_UNSUPPORTED, "decode_explicit: q, C and W^u must be BF16");
+  if (o_dtype != QSVD_BF16 && o_dtype != QSVD_F32)
+    return fail(QSVD_ERR_INVALID, "decode_explicit: o_dtype %s", dtype_name(o_dtype));
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
+    return fail(QSVD_ERR_INVALID, "decode_explicit: softmax_scale must be positive and finite");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(QSVD_ERR_INVALID, "decode_explicit: rope_cos and rope_sin go together");
+  if (!q || !C || !Wk_packed || !Wv_packed || !O)
+    return fail(QSVD_ERR_INVALID, "decode_explicit: NULL pointer");
+  if (!aligned16(q) || !aligned16(C) || !aligned16(Wk_packed) || !aligned16(Wv_packed) ||
+      !aligned16(O) || (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
+      (workspace && !aligned16(workspace)))
+    return fail(QSVD_ERR_INVALID, "decode_explicit: misaligned pointer");
+  const size_t need = qsvd::explicit_workspace_bytes(b, L, heads);
+  if (!workspace || workspace_bytes < need)
+    return fail(QSVD_ERR_WORKSPACE, "decode_explicit: workspace %zu bytes, need %zu",
+                workspace_bytes, need);
+  qsvd::ExplicitArgs a{};
+  a.q = q;
+  a.C = C;
+  a.Wk_t = Wk_packed;
+  a.Wv_t = Wv_packed;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.b = b;
+  a.L = L;
+  a.r = r;
+  a.heads = heads;
+  a.softmax_scale = softmax_scale;
+  a.O = O;
+  a.o_dtype = o_dtype;
+  a.workspace = workspace;
+  return device_status(qsvd::launch_decode_explicit(a, static_cast<hipStream_t>(hip_stream)),
+                       "decode_attn_explicit");
+}
+
 qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *C,
                                qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
                                const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,

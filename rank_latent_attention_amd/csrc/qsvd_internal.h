@@ -40,6 +40,24 @@ hipError_t launch_gemm(const void *A, const float *a_scale, bool int8, int64_t M
 hipError_t launch_transpose(const void *W, int elem_bytes, int rows, int cols, void *out,
                             hipStream_t s);
 
+struct ExplicitArgs {
+  const void *q;        // [b][heads][128] bf16
+  const void *C;        // [b][L][r] bf16
+  const void *Wk_t;     // [E][r] bf16 (W^u_k transposed)
+  const void *Wv_t;     // [E][r] bf16 (W^u_v transposed)
+  const float *rope_cos, *rope_sin;   // [>= L][64] each, or both NULL
+  int b;
+  int64_t L;
+  int r, heads;
+  float softmax_scale;
+  void *O;
+  int o_dtype;
+  void *workspace;
+};
+
+size_t explicit_workspace_bytes(int b, int64_t L, int heads);
+hipError_t launch_decode_explicit(const ExplicitArgs &a, hipStream_t s);
+
 struct DecodeArgs {
   const void *q;
   int q_dtype;

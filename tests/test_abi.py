@@ -149,3 +149,33 @@ def test_timing_session_errors():
     n = ctypes.c_int32(0)
     assert L.qsvd_timing_end(None, 0, ctypes.byref(n)) == -1
     assert L.qsvd_timing_begin(0) == -1
+
+
+def st_exp(**kw):
+    a = dict(q_=FAKE, qdt=q.BF16, C=FAKE, cdt=q.BF16, Wk=FAKE, Wv=FAKE, wdt=q.BF16, b=2, L=300,
+             r=256, heads=4, d=128, scale=0.088, rc=None, rs=None, O=FAKE, odt=q.BF16, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return q.lib().qsvd_decode_attn_explicit(a["q_"], a["qdt"], a["C"], a["cdt"], a["Wk"], a["Wv"],
+                                             a["wdt"], a["b"], a["L"], a["r"], a["heads"], a["d"],
+                                             a["scale"], a["rc"], a["rs"], a["O"], a["odt"], a["ws"],
+                                             a["wsb"], None)
+
+
+def test_decode_explicit_validation():
+    assert st_exp(b=0) == -1
+    assert st_exp(L=0) == -1
+    assert st_exp(d=64) == -2
+    assert st_exp(r=96) == -1                     # r % 64
+    assert st_exp(cdt=q.I8) == -2
+    assert st_exp(wdt=q.I8) == -2
+    assert st_exp(odt=q.I8) == -1
+    assert st_exp(rc=FAKE) == -1                  # the two tables go together
+    assert st_exp(scale=-1.0) == -1
+    assert st_exp(Wv=None) == -1
+    assert st_exp(rc=ctypes.c_void_p((1 << 20) + 4), rs=FAKE) == -1
+    need = q.qsvd_decode_explicit_workspace_bytes(2, 300, 256, 4, 128)
+    # per (sequence, 256-token tile, head): 132 float32
+    assert need == 2 * 2 * 4 * 132 * 4
+    assert st_exp(wsb=need - 1) == -3
+    assert q.qsvd_decode_explicit_workspace_bytes(2, 300, 256, 4, 64) == 0
