@@ -6,6 +6,9 @@ latent-attention layer, E = 4096 (32 heads x 128), r = 1536, b = 16 sequences,
 L = 8192 cached bf16 latents each; the step is qsvd_decode_attn (absorb,
 split-L stream, merge, finalize).  value = decode tokens/s = b / step time.
 
+Explicit leg: the same step with K and V rebuilt explicitly on chip and
+rotary positions (qsvd_decode_attn_explicit), against the bf16 MFMA peak.
+
 Prefill leg: the shared down-projection at W8A8, X [16384][4096] int8 (H1
 rotated, per-token scales) times W^d [4096][1536] int8 (per-column scales),
 reported as TOPS; plus the rotate+quantise steps around it.
@@ -28,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
 COPY_BYTES = 1 << 30  # calibration copy (bytes read = bytes written)
 COUNTERS = os.path.join(ROOT, "profiles", "decode_stream_e4096_r1536_b16_l8192_counters.json")
 
@@ -46,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--chain", action="store_true", help="also time the 24-layer prefill chain")
+    ap.add_argument("--no-explicit", action="store_true",
+                    help="skip the explicit K/V reconstruction (RoPE) decode leg")
     return ap.parse_args()
 
 
@@ -136,6 +142,38 @@ def main():
         if c.get("decode_hip_sha256_16") == kernel_source_hash():
             traffic = c.get("hbm_bytes_per_launch")
 
+    # ------------------------------------------------------------------ explicit K/V leg
+    explicit = None
+    if not args.no_explicit:
+        E = heads * d
+        Wk_t = torch.empty((E, r), dtype=torch.bfloat16, device="cuda")
+        Wv_t = torch.empty((E, r), dtype=torch.bfloat16, device="cuda")
+        q.qsvd_pack_weight(Wk, q.BF16, r, E, Wk_t)
+        q.qsvd_pack_weight(Wv, q.BF16, r, E, Wv_t)
+        rc, rs = (dev(t) for t in synth.rope_tables(L, d))
+        Oe = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
+        ws_e = torch.empty(q.qsvd_decode_explicit_workspace_bytes(b, L, r, heads, d),
+                           dtype=torch.uint8, device="cuda")
+
+        def step_e(i):
+            q.qsvd_decode_attn_explicit(qv, q.BF16, copies[i % len(copies)], q.BF16, Wk_t, Wv_t,
+                                        q.BF16, b, L, r, heads, d, cs.softmax_scale, rc, rs, Oe,
+                                        q.BF16, ws_e)
+
+        ms_e = timed(step_e, max(args.steps // 10, 3), 1)
+        flops = 2.0 * b * L * r * 2 * E
+        tf = flops / (ms_e * 1e-3) / 1e12
+        explicit = {"workload": "same decode step with K_h = C W^u_k,h and V_h = C W^u_v,h rebuilt "
+                                "explicitly on chip and RoPE on keys and query "
+                                "(qsvd_decode_attn_explicit)",
+                    "ms_per_step": round(ms_e, 4), "tokens_per_s": round(b / (ms_e * 1e-3), 1),
+                    "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops},
+                    "latent_path_speedup": round(ms_e / ms, 2)}
+        log(f"[bench] explicit K/V + RoPE decode: {ms_e * 1e3:.1f} us/step, {tf:.0f} TFLOP/s")
+        del ws_e, Wk_t, Wv_t
+
     # ------------------------------------------------------------------ prefill
     prefill = None
     if not args.no_prefill:
@@ -203,6 +241,7 @@ def main():
                      "algorithmic_bytes": cache_bytes},
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "explicit": explicit,
     }
     print(json.dumps(out), flush=True)
 
