@@ -198,14 +198,25 @@ def main():
         t_a1 = timed(a1, steps, 3)
         t_a2 = timed(a2, steps, 3)
         t_a3 = timed(a3, steps, 3)
+        # W4A4: int4 X (a1 with int4 codes) x int4 W^d -> fp32
+        Wd_q4 = np.clip(np.rint(Wd_q.astype(np.float64) / 18.0), -7, 7).astype(np.int8)  # timing-only codes
+        W4 = torch.empty((rp, E // 2), dtype=torch.uint8, device="cuda")
+        q.qsvd_pack_weight(dev(Wd_q4), q.I4, E, rp, W4)
+        x4 = torch.empty((M, E // 2), dtype=torch.uint8, device="cuda")
+        q.qsvd_quantize_latent(Xd, q.BF16, M, E, 128, q.I4, 0, x4, xs)
+        a2_4 = lambda i: q.qsvd_project(x4, q.I4, xs, M, E, W4, q.I4, ws_d, rp, Cp, q.F32)
+        t_a2_4 = timed(a2_4, steps, 3)
+        del W4, x4
         tops = 2.0 * M * E * rp / (t_a2 * 1e-3) / 1e12
         prefill = {"workload": "X[16384][4096] int8 x W^d[4096][1536] int8 -> fp32",
                    "proj_us": round(t_a2 * 1e3, 2), "proj_tops": round(tops, 1),
                    "peak_tops": INT8_PEAK_TOPS, "frac": round(tops / INT8_PEAK_TOPS, 4),
+                   "w4a4_proj_us": round(t_a2_4 * 1e3, 2),
+                   "w4a4_proj_tops": round(2.0 * M * E * rp / (t_a2_4 * 1e-3) / 1e12, 1),
                    "rotate_quant_x_us": round(t_a1 * 1e3, 2),
                    "rotate_quant_c_us": round(t_a3 * 1e3, 2)}
         log(f"[bench] prefill: a1 {t_a1 * 1e3:.1f} us, a2 {t_a2 * 1e3:.1f} us ({tops:.0f} TOPS), "
-            f"a3 {t_a3 * 1e3:.1f} us")
+            f"a3 {t_a3 * 1e3:.1f} us; W4A4 a2 {t_a2_4 * 1e3:.1f} us")
         if args.chain:
             prefill["chain"] = chain_leg(q, torch, np, synth, xq, xs, M, E, steps=3)
         del Xd, xq, Cp, cq

@@ -92,17 +92,22 @@ qsvd_status_t qsvd_quantize_latent(const void *in, qsvd_dtype_t in_dtype, int64_
  * ([K | V] = C [W^u_k | W^u_v]) when E is read as the latent width r and r
  * as the output width.
  *
- *   X          [M][E]  I8 codes with x_scale float32 [M], or BF16 (x_scale NULL).
+ *   X          [M][E]  I8 codes with x_scale float32 [M]; or I4 codes packed
+ *              two per byte ([M][E/2], element 2j in the low nibble of byte
+ *              j, as qsvd_quantize_latent writes them) with x_scale [M]; or
+ *              BF16 (x_scale NULL).
  *   W_packed   [r][E]  the weight W^d (E x r) stored transposed, i.e. each
- *              output column contiguous along E; see qsvd_pack_weight.
- *              w_dtype must equal x_dtype.
+ *              output column contiguous along E ([r][E/2] packed for I4);
+ *              see qsvd_pack_weight.  w_dtype must equal x_dtype.
  *   col_scale  float32 [r] per-output-column weight scale, or NULL (= 1).
  *              Sigma_r^beta is folded into W^d before its quantisation.
  *   C          [M][r]  F32 or BF16.
- *   int8:  acc = sum_k X[m][k] W[k][n] (exact int32);
+ *   int8 and int4 (W4A4, QSVD paper notes "Main results"):
+ *          acc = sum_k X[m][k] W[k][n] (exact int32);
  *          C[m][n] = float32(float32(float32(acc) * x_scale[m]) * col_scale[n]).
  *   bf16:  C[m][n] = (sum_k X[m][k] W[k][n]) * col_scale[n], float32 accumulation.
- *   Constraints: E % 64 == 0, r % 16 == 0, M >= 0 (M == 0 is a no-op).
+ *   Constraints: E % 64 == 0 (E % 128 == 0 for I4), r % 16 == 0, M >= 0
+ *   (M == 0 is a no-op).
  */
 qsvd_status_t qsvd_project(const void *X, qsvd_dtype_t x_dtype, const float *x_scale, int64_t M,
                            int32_t E, const void *W_packed, qsvd_dtype_t w_dtype,
@@ -111,7 +116,10 @@ qsvd_status_t qsvd_project(const void *X, qsvd_dtype_t x_dtype, const float *x_s
 
 /*
  * Transpose a weight [rows][cols] -> [cols][rows] (the W_packed layout of
- * qsvd_project).  dt: F32, BF16 or I8.  Offline, not on the hot path.
+ * qsvd_project).  dt: F32, BF16 or I8.  For I4, W holds int8 codes in
+ * [-8, 7] (one per byte, [rows][cols], rows even) and packed receives
+ * [cols][rows / 2] with codes k and k + 1 of a column in the low and high
+ * nibble of one byte.  Offline, not on the hot path.
  */
 qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int32_t cols,
                                void *packed, void *hip_stream);

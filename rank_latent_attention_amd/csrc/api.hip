@@ -128,8 +128,8 @@ qsvd_status_t qsvd_project(const void *X, qsvd_dtype_t x_dtype, const float *x_s
                            int32_t E, const void *W_packed, qsvd_dtype_t w_dtype,
                            const float *col_scale, int32_t r, void *C, qsvd_dtype_t c_dtype,
                            void *hip_stream) {
-  if (x_dtype != QSVD_I8 && x_dtype != QSVD_BF16)
-    return fail(QSVD_ERR_UNSUPPORTED, "project: x_dtype %s (I8 or BF16)", dtype_name(x_dtype));
+  if (x_dtype != QSVD_I8 && x_dtype != QSVD_I4 && x_dtype != QSVD_BF16)
+    return fail(QSVD_ERR_UNSUPPORTED, "project: x_dtype %s (I8, I4 or BF16)", dtype_name(x_dtype));
   if (w_dtype != x_dtype)
     return fail(QSVD_ERR_UNSUPPORTED, "project: w_dtype %s must equal x_dtype %s",
                 dtype_name(w_dtype), dtype_name(x_dtype));
@@ -140,8 +140,10 @@ qsvd_status_t qsvd_project(const void *X, qsvd_dtype_t x_dtype, const float *x_s
     return fail(QSVD_ERR_INVALID, "project: E = %d (positive multiple of 64)", E);
   if (r <= 0 || r % 16 != 0)
     return fail(QSVD_ERR_INVALID, "project: r = %d (positive multiple of 16)", r);
-  if (x_dtype == QSVD_I8 && !x_scale)
-    return fail(QSVD_ERR_INVALID, "project: int8 X needs x_scale");
+  if (x_dtype == QSVD_I4 && E % 128 != 0)
+    return fail(QSVD_ERR_INVALID, "project: int4 operands need E %% 128 == 0 (E = %d)", E);
+  if ((x_dtype == QSVD_I8 || x_dtype == QSVD_I4) && !x_scale)
+    return fail(QSVD_ERR_INVALID, "project: integer X needs x_scale");
   if (x_dtype == QSVD_BF16 && x_scale)
     return fail(QSVD_ERR_INVALID, "project: bf16 X takes no x_scale");
   if (M == 0) return ok();
@@ -151,7 +153,8 @@ qsvd_status_t qsvd_project(const void *X, qsvd_dtype_t x_dtype, const float *x_s
     return fail(QSVD_ERR_INVALID, "project: misaligned pointer");
   const int64_t tiles = ((M + 127) / 128) * ((r + 127) / 128);
   if (tiles > 0x7FFFFFFF) return fail(QSVD_ERR_INVALID, "project: problem too large");
-  const hipError_t e = qsvd::launch_gemm(X, x_scale, x_dtype == QSVD_I8, M, E, W_packed, col_scale,
+  const int kind = x_dtype == QSVD_I4 ? qsvd::kGemmI4 : (x_dtype == QSVD_I8 ? qsvd::kGemmI8 : qsvd::kGemmBF16);
+  const hipError_t e = qsvd::launch_gemm(X, x_scale, kind, M, E, W_packed, col_scale,
                                          r, C, c_dtype == QSVD_BF16,
                                          static_cast<hipStream_t>(hip_stream));
   return device_status(e, "project");
@@ -164,11 +167,18 @@ qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int
     case QSVD_F32: esz = 4; break;
     case QSVD_BF16: esz = 2; break;
     case QSVD_I8: esz = 1; break;
+    case QSVD_I4: esz = 0; break;
     default: return fail(QSVD_ERR_INVALID, "pack_weight: dtype %s", dtype_name(dt));
   }
   if (rows < 0 || cols < 0) return fail(QSVD_ERR_INVALID, "pack_weight: negative shape");
+  if (dt == QSVD_I4 && rows % 2 != 0)
+    return fail(QSVD_ERR_INVALID, "pack_weight: I4 needs an even row count (rows = %d)", rows);
   if (rows == 0 || cols == 0) return ok();
   if (!W || !packed) return fail(QSVD_ERR_INVALID, "pack_weight: NULL pointer");
+  if (dt == QSVD_I4)
+    return device_status(qsvd::launch_pack_int4(W, rows, cols, packed,
+                                                static_cast<hipStream_t>(hip_stream)),
+                         "pack_weight");
   return device_status(qsvd::launch_transpose(W, esz, rows, cols, packed,
                                               static_cast<hipStream_t>(hip_stream)),
                        "pack_weight");

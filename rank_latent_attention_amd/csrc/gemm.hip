@@ -43,7 +43,7 @@ using dma::wait_all_loads;
 constexpr int kComputeUnits = 256;       // gfx950: 8 XCDs x 32 CUs
 constexpr int kEpiStride = 36;           // epilogue block row stride (32-bit words)
 
-template <bool INT8, bool OUT_BF16, int BM, int BN, int WM, int WN>
+template <bool INT8, bool OUT_BF16, int BM, int BN, int WM, int WN, bool INT4>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scale, int64_t M, int K,
                  const uint8_t *__restrict__ Bt, const float *__restrict__ col_scale, int N,
@@ -60,7 +60,8 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
   static_assert(1024 + NW * 32 * kEpiStride * 4 <= 2 * SLOT, "epilogue fits in the slots");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
-  const int64_t kbytes = static_cast<int64_t>(K) * (INT8 ? 1 : 2);
+  static_assert(INT8 || !INT4, "int4 operands are integer codes");
+  const int64_t kbytes = INT4 ? static_cast<int64_t>(K) / 2 : static_cast<int64_t>(K) * (INT8 ? 1 : 2);
   const int nbn = (N + BN - 1) / BN;
   const int total = gridDim.x, id = blockIdx.x;
   const int per = total / 8, rem = total % 8;
@@ -147,24 +148,56 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
 #pragma unroll
       for (int q = 0; q < PER; ++q)
         if (ks * PER + q < LPW) issue_one(ks * PER + q, nstage, nslot);
+      if constexpr (INT4) {
+        // 16 bytes = 32 int4 codes.  Masking a nibble into the high half of
+        // its byte gives the int8 value 16 * code, exactly: the odd elements
+        // (high nibbles) and the even ones (shifted up) form two int8
+        // operands; A and B pair them the same way, so the sum over K is
+        // unchanged and the int32 accumulator holds 256 * sum exactly.
+        u32x4 blo[NB];
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if constexpr (INT8)
+          for (int e = 0; e < 4; ++e) {
+            blo[j][e] = (bfr[j][e] << 4) & 0xF0F0F0F0u;
+            bfr[j][e] &= 0xF0F0F0F0u;
+          }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          u32x4 alo, ahi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            alo[e] = (af[i][e] << 4) & 0xF0F0F0F0u;
+            ahi[e] = af[i][e] & 0xF0F0F0F0u;
+          }
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                __builtin_bit_cast(i32x4, af[i]), __builtin_bit_cast(i32x4, bfr[j]), acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+                __builtin_bit_cast(i32x4, alo), __builtin_bit_cast(i32x4, blo[j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                __builtin_bit_cast(i32x4, ahi), __builtin_bit_cast(i32x4, bfr[j]), acc[i][j], 0, 0, 0);
+          }
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            if constexpr (INT8)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                  __builtin_bit_cast(i32x4, af[i]), __builtin_bit_cast(i32x4, bfr[j]), acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+          }
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, MB + NB, 0);   // LDS operand reads
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // 2 MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // 1 DMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);   // the remaining MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB * (INT4 ? 2 : 1), 0);   // the remaining MFMAs
     }
   };
 
@@ -222,7 +255,8 @@ void gemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ a_scal
         for (int c = 0; c < 4; ++c) {
           const uint32_t wc = w[c];
           if constexpr (INT8) {
-            v[c] = static_cast<float>(static_cast<int>(wc));
+            // int4: the accumulator is 256 * the integer sum (a multiple of 256)
+            v[c] = static_cast<float>(INT4 ? (static_cast<int>(wc) >> 8) : static_cast<int>(wc));
             v[c] = v[c] * las[lrow];
             v[c] = v[c] * csr[j][c];
           } else {
@@ -261,12 +295,12 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in
   }
 }
 
-template <bool INT8, bool OUT_BF16, int BM, int BN, int WM, int WN>
+template <bool INT8, bool OUT_BF16, int BM, int BN, int WM, int WN, bool INT4>
 hipError_t run_gemm(const uint8_t *a, const float *a_scale, int64_t M, int K, const uint8_t *b,
                     const float *col_scale, int N, void *C, hipStream_t s) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   constexpr size_t lds = static_cast<size_t>(2) * (BM + BN) * BK;
-  auto kern = gemm_kernel<INT8, OUT_BF16, BM, BN, WM, WN>;
+  auto kern = gemm_kernel<INT8, OUT_BF16, BM, BN, WM, WN, INT4>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
@@ -275,7 +309,7 @@ hipError_t run_gemm(const uint8_t *a, const float *a_scale, int64_t M, int K, co
   return hipGetLastError();
 }
 
-template <bool INT8, bool OUT_BF16>
+template <bool INT8, bool OUT_BF16, bool INT4 = false>
 hipError_t run_gemm_shape(const uint8_t *a, const float *a_scale, int64_t M, int K,
                           const uint8_t *b, const float *col_scale, int N, void *C,
                           hipStream_t s) {
@@ -285,37 +319,66 @@ hipError_t run_gemm_shape(const uint8_t *a, const float *a_scale, int64_t M, int
   // (256 tiles, one round); 16384 x 512 -> 128 x 256; 16384 x 8192 -> 256 x 256.
   struct Cand { int bm, bn, per_cu; };
   static constexpr Cand cands[] = {{256, 384, 1}, {256, 256, 1}, {128, 256, 1}, {128, 128, 2}};
-  int best = 0;
+  int best = INT4 ? 1 : 0;
   int64_t best_cost = INT64_MAX;
-  for (int i = 0; i < 4; ++i) {
+  // (int4 unpacking needs registers the 256 x 384 accumulators leave no room for)
+  for (int i = INT4 ? 1 : 0; i < 4; ++i) {
     const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
     const int64_t slots = static_cast<int64_t>(kComputeUnits) * cands[i].per_cu;
     const int64_t cost = ((tiles + slots - 1) / slots) * cands[i].bm * cands[i].bn * cands[i].per_cu;
     if (cost < best_cost) { best_cost = cost; best = i; }
   }
   switch (best) {
-    case 0: return run_gemm<INT8, OUT_BF16, 256, 384, 2, 4>(a, a_scale, M, K, b, col_scale, N, C, s);
-    case 1: return run_gemm<INT8, OUT_BF16, 256, 256, 2, 4>(a, a_scale, M, K, b, col_scale, N, C, s);
-    case 2: return run_gemm<INT8, OUT_BF16, 128, 256, 2, 4>(a, a_scale, M, K, b, col_scale, N, C, s);
-    default: return run_gemm<INT8, OUT_BF16, 128, 128, 2, 2>(a, a_scale, M, K, b, col_scale, N, C, s);
+    case 0:
+      if constexpr (!INT4) return run_gemm<INT8, OUT_BF16, 256, 384, 2, 4, false>(a, a_scale, M, K, b, col_scale, N, C, s);
+      [[fallthrough]];
+    case 1: return run_gemm<INT8, OUT_BF16, 256, 256, 2, 4, INT4>(a, a_scale, M, K, b, col_scale, N, C, s);
+    case 2: return run_gemm<INT8, OUT_BF16, 128, 256, 2, 4, INT4>(a, a_scale, M, K, b, col_scale, N, C, s);
+    default: return run_gemm<INT8, OUT_BF16, 128, 128, 2, 2, INT4>(a, a_scale, M, K, b, col_scale, N, C, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const void *A, const float *a_scale, bool int8, int64_t M, int K,
+hipError_t launch_gemm(const void *A, const float *a_scale, int in_kind, int64_t M, int K,
                        const void *Bt, const float *col_scale, int N, void *C, bool c_bf16,
                        hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   const auto *a = static_cast<const uint8_t *>(A);
   const auto *b = static_cast<const uint8_t *>(Bt);
-  LaunchTimer t(int8 ? "gemm_i8" : "gemm_bf16", s);
-  if (int8) {
+  LaunchTimer t(in_kind == kGemmI4 ? "gemm_i4" : (in_kind == kGemmI8 ? "gemm_i8" : "gemm_bf16"), s);
+  if (in_kind == kGemmI4) {
+    if (c_bf16) return run_gemm_shape<true, true, true>(a, a_scale, M, K, b, col_scale, N, C, s);
+    return run_gemm_shape<true, false, true>(a, a_scale, M, K, b, col_scale, N, C, s);
+  }
+  if (in_kind == kGemmI8) {
     if (c_bf16) return run_gemm_shape<true, true>(a, a_scale, M, K, b, col_scale, N, C, s);
     return run_gemm_shape<true, false>(a, a_scale, M, K, b, col_scale, N, C, s);
   }
   if (c_bf16) return run_gemm_shape<false, true>(a, a_scale, M, K, b, col_scale, N, C, s);
   return run_gemm_shape<false, false>(a, a_scale, M, K, b, col_scale, N, C, s);
+}
+
+// packed[c][k / 2] = code[k][c] (low nibble) | code[k + 1][c] << 4, from int8 codes [rows][cols]
+__global__ __launch_bounds__(256) void pack_int4_transpose_kernel(const int8_t *__restrict__ in,
+                                                                  int rows, int cols,
+                                                                  uint8_t *__restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int half = rows / 2;
+  if (i >= static_cast<int64_t>(cols) * half) return;
+  const int c = static_cast<int>(i / half), k2 = static_cast<int>(i % half);
+  const int lo = in[static_cast<int64_t>(2 * k2) * cols + c] & 0xF;
+  const int hi = in[static_cast<int64_t>(2 * k2 + 1) * cols + c] & 0xF;
+  out[i] = static_cast<uint8_t>(lo | (hi << 4));
+}
+
+hipError_t launch_pack_int4(const void *W, int rows, int cols, void *out, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const int64_t n = static_cast<int64_t>(cols) * (rows / 2);
+  LaunchTimer t("pack_int4", s);
+  pack_int4_transpose_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(
+      static_cast<const int8_t *>(W), rows, cols, static_cast<uint8_t *>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_transpose(const void *W, int elem_bytes, int rows, int cols, void *out,

@@ -33,9 +33,14 @@ hipError_t launch_rotate_quant(const void *in, bool in_bf16, int64_t M, int n, b
                                bool int4, bool grouped, void *codes, float *scales,
                                hipStream_t s);
 
-hipError_t launch_gemm(const void *A, const float *a_scale, bool int8, int64_t M, int K,
+// in_kind: operand format of A and B (bf16, int8 codes, packed int4 codes)
+enum : int { kGemmBF16 = 0, kGemmI8 = 1, kGemmI4 = 2 };
+hipError_t launch_gemm(const void *A, const float *a_scale, int in_kind, int64_t M, int K,
                        const void *Bt, const float *col_scale, int N, void *C, bool c_bf16,
                        hipStream_t s);
+
+// transpose int8 codes [rows][cols] into packed int4 [cols][rows / 2]
+hipError_t launch_pack_int4(const void *W, int rows, int cols, void *out, hipStream_t s);
 
 hipError_t launch_transpose(const void *W, int elem_bytes, int rows, int cols, void *out,
                             hipStream_t s);

@@ -42,7 +42,7 @@ __all__ = [
     "activations", "Layer", "make_layer", "block_hadamard", "to_bf16_bits",
     "bf16_bits_to_f64", "int8_columns", "decode_case", "DecodeCase",
     "c4_ranks", "c4_layer", "sharpen_query", "quant_decode_inputs", "QuantDecodeInputs",
-    "rope_tables",
+    "rope_tables", "int4_columns",
 ]
 
 
@@ -403,3 +403,14 @@ def rope_tables(P: int, d: int, base: float = 10000.0):
     i = np.arange(d // 2, dtype=np.float64)
     a = np.arange(P, dtype=np.float64)[:, None] * (base ** (-2.0 * i / d))[None, :]
     return np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
+
+
+def int4_columns(W: np.ndarray):
+    """Offline symmetric per-column int4 weight codes (W4A4): (codes int8 in [-7, 7]
+    [rows][cols], scale f32 [cols]); scale = max_k |W[k, n]| / 7, code = rint(W / scale)."""
+    W = np.asarray(W, dtype=np.float64)
+    scale = (np.abs(W).max(axis=0) / 7.0).astype(np.float32)
+    s64 = scale.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s64 > 0, np.rint(W / np.where(s64 > 0, s64, 1.0)), 0.0)
+    return np.clip(q, -7, 7).astype(np.int8), scale

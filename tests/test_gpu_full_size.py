@@ -178,3 +178,30 @@ def test_prefill_full_size_sampled_rows():
     ref = oracle.bf16_round(oracle.project_int8(c3, s3, Wkv, skv))
     assert np.array_equal(host(KV[ridx]), ref)
     say(f"  r = {rl} layer: a2, a3, a4 rows bit-exact")
+
+
+def test_prefill_w4a4_full_size_sampled_rows():
+    """W4A4 at the 16384 x 4096 -> 1536 shape: X rotated by H1 and quantised to
+    int4 per token (a1), the int4 x int4 projection (a2), sampled rows
+    bit-exact against the oracle chain."""
+    import torch
+    M, E, r = 4 * 4096, 4096, 1536
+    say(f"case: full-size W4A4 prefill M={M} E={E} r={r}")
+    X = synth.to_bf16_bits(synth.prefill_activations(M, E))
+    rows = np.unique(np.concatenate([[0, 1, M - 1], np.random.default_rng(6).integers(M, size=21)]))
+    xq = empty((M, E // 2), torch.uint8)
+    xs = empty((M,), torch.float32)
+    q.qsvd_quantize_latent(dev(X), q.BF16, M, E, 128, q.I4, 0, xq, xs)
+    c1, s1 = oracle.rotate_quantize(oracle.bf16_decode(X[rows]), 128, 4, 0)
+    del X
+    ridx = torch.from_numpy(rows).cuda()
+    assert np.array_equal(oracle.unpack_int4(xq[ridx].cpu().numpy()), c1)
+    assert np.array_equal(xs[ridx].cpu().numpy(), s1)
+    lay = synth.c4_layer(0, r)
+    Wd_q4, Wd_s4 = synth.int4_columns(oracle.dequant_cols(lay["Wd_q"], lay["Wd_s"]))
+    Wp = empty((r, E // 2), torch.uint8)
+    q.qsvd_pack_weight(dev(Wd_q4), q.I4, E, r, Wp)
+    Cp = empty((M, r), torch.float32)
+    q.qsvd_project(xq, q.I4, xs, M, E, Wp, q.I4, dev(Wd_s4), r, Cp, q.F32)
+    assert np.array_equal(host(Cp[ridx]), oracle.project_int8(c1, s1, Wd_q4, Wd_s4))
+    say("  a1 (int4) and a2 (W4A4) rows bit-exact")

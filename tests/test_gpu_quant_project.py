@@ -156,6 +156,51 @@ def test_project_bf16(M, K, N):
     assert oracle.rel_l2(got, ref) < 1e-5
 
 
+def run_project_i4(A, sa, W, sw, out_bf16=False):
+    """A int8 codes [M][K] (int4 range), W int8 codes [K][N]; X packed on the host,
+    W packed by qsvd_pack_weight (checked against the host packing)."""
+    import torch
+    M, K = A.shape
+    N = W.shape[1]
+    Wp = empty((N, K // 2), torch.uint8)
+    q.qsvd_pack_weight(dev(W), q.I4, K, N, Wp)
+    torch.cuda.synchronize()
+    assert np.array_equal(Wp.cpu().numpy(), oracle.pack_int4(np.ascontiguousarray(W.T)))
+    C = empty((M, N), torch.bfloat16 if out_bf16 else torch.float32)
+    q.qsvd_project(dev(oracle.pack_int4(A)), q.I4, dev(sa), M, K, Wp, q.I4,
+                   dev(sw) if sw is not None else None, N, C, q.BF16 if out_bf16 else q.F32)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (77, 1152, 48), (257, 4096, 1536), (130, 512, 272),
+                                   (300, 2048, 8192), (1000, 4096, 400)])
+def test_project_int4_bit_exact(M, K, N):
+    say(f"case: project W4A4 M={M} K={K} N={N}")
+    g = np.random.default_rng(M + 3 * K + N)
+    A = g.integers(-8, 8, size=(M, K)).astype(np.int8)      # the full nibble range
+    W = g.integers(-8, 8, size=(K, N)).astype(np.int8)
+    sa = (g.random(M) * 1e-2 + 1e-4).astype(np.float32)
+    sw = (g.random(N) * 1e-2 + 1e-4).astype(np.float32)
+    C = host(run_project_i4(A, sa, W, sw))
+    assert np.array_equal(C, oracle.project_int8(A, sa, W, sw))
+    # extreme sums: all -8 * -8
+    A2 = np.full((3, K), -8, np.int8)
+    W2 = np.full((K, 16), -8, np.int8)
+    C2 = host(run_project_i4(A2, np.ones(3, np.float32), W2, None))
+    assert np.array_equal(C2, oracle.project_int8(A2, np.ones(3, np.float32), W2, np.ones(16)))
+
+
+def test_project_int4_bf16_output():
+    g = np.random.default_rng(8)
+    A = g.integers(-7, 8, size=(100, 256)).astype(np.int8)
+    W = g.integers(-7, 8, size=(256, 64)).astype(np.int8)
+    sa = (g.random(100) * 1e-2).astype(np.float32)
+    sw = (g.random(64) * 1e-2).astype(np.float32)
+    C = run_project_i4(A, sa, W, sw, out_bf16=True)
+    assert np.array_equal(host(C), oracle.bf16_round(oracle.project_int8(A, sa, W, sw)))
+
+
 def test_pack_weight_transposes():
     import torch
     g = np.random.default_rng(0)
