@@ -458,6 +458,43 @@ def attend_explicit_rope(q, C, Wu_k, Wu_v, heads: int, d: int, softmax_scale: fl
     return out
 
 
+# ----------------------------------------------------------------------------
+# Per-head latents (WSVD decode)
+# ----------------------------------------------------------------------------
+
+
+def attend_headwise(q, CK, CV, BK, BV, softmax_scale: float, base: float | None = None) -> np.ndarray:
+    """Decode attention over per-head latents ([WSVD-digest] "Method, 3.1"
+    per-head SVD W_Kh = A_Kh B_Kh with the per-head latent C_Kh = X A_Kh, and
+    "Method, 3.4" the fused decode that rebuilds K_{h,t} = C_{Kh,t} B_{Kh}).
+    With V the same way (C_Vh, B_Vh), for every sequence b and head h:
+        K_h = CK[b, :, h] BK[h],  V_h = CV[b, :, h] BV[h],
+        s = softmax_scale * rope(K_h[t], t) . rope(q_h, L - 1)   (no rotation if base is None),
+        o_{b,h} = softmax(s)^T V_h.
+    q [b][heads][d]; CK [b][L][heads][rk]; CV [b][L][heads][rv]; BK [heads][rk][d];
+    BV [heads][rv][d].  Returns O [b][heads][d] (float64).
+    Pinned by the block-diagonal form: the same attention through
+    attend_explicit / attend_explicit_rope with the latents of all heads
+    concatenated and W^u_k, W^u_v block-diagonal in the heads."""
+    q = np.asarray(q, np.float64)
+    CK = np.asarray(CK, np.float64)
+    CV = np.asarray(CV, np.float64)
+    BK = np.asarray(BK, np.float64)
+    BV = np.asarray(BV, np.float64)
+    b, L, heads = CK.shape[0], CK.shape[1], CK.shape[2]
+    out = np.empty((b, heads, q.shape[2]))
+    for s in range(b):
+        for h in range(heads):
+            K = CK[s, :, h] @ BK[h]
+            V = CV[s, :, h] @ BV[h]
+            qh = q[s, h]
+            if base is not None:
+                K = rope_rotate(K, np.arange(L), base)
+                qh = rope_rotate(qh, L - 1, base)
+            out[s, h] = _softmax(softmax_scale * (K @ qh)) @ V
+    return out
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

@@ -42,7 +42,7 @@ __all__ = [
     "activations", "Layer", "make_layer", "block_hadamard", "to_bf16_bits",
     "bf16_bits_to_f64", "int8_columns", "decode_case", "DecodeCase",
     "c4_ranks", "c4_layer", "sharpen_query", "quant_decode_inputs", "QuantDecodeInputs",
-    "rope_tables", "int4_columns",
+    "rope_tables", "int4_columns", "headwise_case", "HeadwiseCase",
 ]
 
 
@@ -414,3 +414,58 @@ def int4_columns(W: np.ndarray):
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.where(s64 > 0, np.rint(W / np.where(s64 > 0, s64, 1.0)), 0.0)
     return np.clip(q, -7, 7).astype(np.int8), scale
+
+
+# ----------------------------------------------------------------------------
+# Per-head latent caches (the WSVD decode workload)
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class HeadwiseCase:
+    """Inputs of a per-head-latent decode step, bf16 bit patterns.
+
+    C     [b][L][heads][rk + rv]   each head's key latent, then its value latent
+    q     [b][heads][d]
+    BK_t  [heads][d][rk]           B_Kh transposed (contiguous along the latent)
+    BV    [heads][rv][d]
+    """
+    b: int
+    L: int
+    heads: int
+    d: int
+    rk: int
+    rv: int
+    q: np.ndarray
+    C: np.ndarray
+    BK_t: np.ndarray
+    BV: np.ndarray
+    softmax_scale: float
+
+
+def headwise_case(b: int, L: int, heads: int, d: int, rk: int, rv: int, *, p: float = 0.5,
+                  beta: float = 0.5, seed: int = 41, seqs=None) -> HeadwiseCase:
+    """Seeded per-head factors B_Kh = sigma^(1-beta) V_h^T (Haar V_h, sigma_i = i^-p)
+    and latents whose column i has scale sigma_i^beta (the A_Kh = U sigma^beta side
+    applied to unit-variance activations), 1% of latent columns x8; the query of a
+    sequence is Gaussian x 2.  ``seqs`` restricts generation to a subset of
+    sequences (same values as in the full batch)."""
+    sig = spectrum(p, d)
+    BK = np.stack([(sig[:rk] ** (1 - beta))[:, None] * haar_columns(d, rk, rng(seed, _V, h)).T
+                   for h in range(heads)])                                   # [heads][rk][d]
+    BV = np.stack([(sig[:rv] ** (1 - beta))[:, None] * haar_columns(d, rv, rng(seed, _U, h)).T
+                   for h in range(heads)])
+    colk = np.tile(sig[:rk] ** beta, heads)
+    colv = np.tile(sig[:rv] ** beta, heads)
+    out_ch = outlier_channels(heads * (rk + rv), 0.01, rng(seed, _OUTLIER))
+    seqs = range(b) if seqs is None else seqs
+    Cs, qs = [], []
+    for s in seqs:
+        g = rng(seed, _X, s)
+        z = g.standard_normal((L, heads * (rk + rv)))
+        z[:, out_ch] *= 8.0
+        ck = z[:, : heads * rk] * colk
+        cv = z[:, heads * rk:] * colv
+        Cs.append(np.concatenate([ck.reshape(L, heads, rk), cv.reshape(L, heads, rv)], axis=2))
+        qs.append(rng(seed, _XNEW, s).standard_normal((heads, d)) * 2.0)
+    return HeadwiseCase(len(qs), L, heads, d, rk, rv, to_bf16_bits(np.stack(qs)),
+                        to_bf16_bits(np.stack(Cs)), to_bf16_bits(np.ascontiguousarray(BK.transpose(0, 2, 1))),
+                        to_bf16_bits(BV), 1.0 / math.sqrt(d))

@@ -347,3 +347,45 @@ def test_rope_attention_relative_positions_and_l1():
     a1 = oracle.attend_explicit_rope(q, C[:, :1], cs.Wu_k, cs.Wu_v, 2, 128, cs.softmax_scale, pos0=5)
     p1 = oracle.attend_explicit(q, C[:, :1], cs.Wu_k, cs.Wu_v, 2, 128, cs.softmax_scale)
     assert oracle.rel_l2(a1, p1) < 1e-13
+
+
+# ------------------------------------------------------------------ per-head latents
+@pytest.mark.parametrize("base", [None, 10000.0])
+def test_headwise_equals_block_diagonal_shared_latent(base):
+    """Per-head latents are the shared-latent attention with the heads' latents
+    concatenated and W^u block-diagonal: the two oracle paths must agree."""
+    g = np.random.default_rng(31)
+    b, L, heads, d, rk, rv = 2, 37, 3, 16, 5, 7
+    q = g.standard_normal((b, heads, d))
+    CK = g.standard_normal((b, L, heads, rk))
+    CV = g.standard_normal((b, L, heads, rv))
+    BK = g.standard_normal((heads, rk, d)) / math.sqrt(rk)
+    BV = g.standard_normal((heads, rv, d)) / math.sqrt(rv)
+    got = oracle.attend_headwise(q, CK, CV, BK, BV, 0.3, base)
+    C = np.concatenate([CK.reshape(b, L, heads * rk), CV.reshape(b, L, heads * rv)], axis=2)
+    Wk = np.zeros((heads * (rk + rv), heads * d))
+    Wv = np.zeros_like(Wk)
+    for h in range(heads):
+        Wk[h * rk:(h + 1) * rk, h * d:(h + 1) * d] = BK[h]
+        Wv[heads * rk + h * rv: heads * rk + (h + 1) * rv, h * d:(h + 1) * d] = BV[h]
+    if base is None:
+        want = oracle.attend_explicit(q, C, Wk, Wv, heads, d, 0.3)
+    else:
+        want = oracle.attend_explicit_rope(q, C, Wk, Wv, heads, d, 0.3, base)
+    assert oracle.rel_l2(got, want) < 1e-12
+
+
+def test_headwise_full_rank_identity_is_plain_attention():
+    """rk = rv = d with B = I: keys and values are the latents themselves."""
+    g = np.random.default_rng(32)
+    b, L, heads, d = 1, 20, 2, 8
+    q = g.standard_normal((b, heads, d))
+    K = g.standard_normal((b, L, heads, d))
+    V = g.standard_normal((b, L, heads, d))
+    eye = np.stack([np.eye(d)] * heads)
+    got = oracle.attend_headwise(q, K, V, eye, eye, 1 / math.sqrt(d))
+    for h in range(heads):
+        s = K[0, :, h] @ q[0, h] / math.sqrt(d)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        assert np.allclose(got[0, h], p @ V[0, :, h], atol=1e-13)
