@@ -219,6 +219,54 @@ qsvd_status_t qsvd_decode_attn_explicit(const void *q, qsvd_dtype_t q_dtype, con
                                         void *workspace, size_t workspace_bytes,
                                         void *hip_stream);
 
+/*
+ * qsvd_decode_attn_headwise: decode over per-head latents.  Each head h has
+ * its own factors W_Kh = A_Kh B_Kh and W_Vh = A_Vh B_Vh, and the cache holds
+ * the per-head latents C_Kh = X A_Kh (rk values per token) and C_Vh = X A_Vh
+ * (rv values).  For every sequence and head:
+ *   K_h = C_Kh B_Kh (rebuilt tile by tile on chip, never written out),
+ *   s_t = softmax_scale * rope(K_h[t], t) . rope(q_h, L - 1),
+ *   o_h = (softmax(s)^T C_Vh) B_Vh   (B_Vh applied once, after the softmax).
+ *
+ * Passage: WSVD digest, "Method, 3.1" (per-head low-rank factors and
+ * per-head latent caches) and "Method, 3.4" (the fused flash-decoding pass:
+ * latent tiles streamed on chip, K rebuilt in registers with RoPE, B_Vh
+ * folded into the output side).
+ *
+ *   q          [b][heads][d] bf16; d must be 128.
+ *   C          [b][L][heads][rk + rv] bf16: per token and head, the key latent
+ *              (rk values) followed by the value latent (rv values).
+ *   BK_t       [heads][d][rk] bf16: B_Kh transposed (contiguous along the latent).
+ *   BV         [heads][rv][d] bf16: B_Vh as is.
+ *   rk, rv     each 32, 64, 96 or 128.
+ *   rope_cos, rope_sin
+ *              NULL (no rotation) or float32 tables [P][d/2], P >= L, with the
+ *              same meaning and rotation as in qsvd_decode_attn_explicit
+ *              (cached token t at position t, the query at L - 1).
+ *   splits     L-splits per sequence (0: a default that fills the device;
+ *              at most 1024, clipped to the number of 32-token tiles).
+ *   O          [b][heads][d], o_dtype BF16 or F32.
+ *   workspace  qsvd_decode_headwise_workspace_bytes(...) bytes, 16-byte aligned
+ *              (per (sequence, split, head): running max, sum and the
+ *              rv-wide unnormalised softmax(s)^T C_Vh, float32).
+ * All pointers are device memory owned by the caller and 16-byte aligned.
+ * Errors: QSVD_ERR_UNSUPPORTED for dtypes other than bf16, d != 128 or a rank
+ * outside {32, 64, 96, 128}; QSVD_ERR_INVALID for bad shapes / pointers / a
+ * lone RoPE table; QSVD_ERR_WORKSPACE for a short workspace.  Nothing is
+ * launched on error; the workspace size query returns 0 for invalid shapes.
+ */
+size_t qsvd_decode_headwise_workspace_bytes(int32_t b, int64_t L, int32_t heads, int32_t d,
+                                            int32_t rk, int32_t rv, int32_t splits);
+
+qsvd_status_t qsvd_decode_attn_headwise(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                        qsvd_dtype_t c_dtype, const void *BK_t, const void *BV,
+                                        qsvd_dtype_t b_dtype, int32_t b, int64_t L, int32_t heads,
+                                        int32_t d, int32_t rk, int32_t rv, float softmax_scale,
+                                        const float *rope_cos, const float *rope_sin,
+                                        int32_t splits, void *O, qsvd_dtype_t o_dtype,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *hip_stream);
+
 /* The split count qsvd_decode_attn uses when called with splits == 0. */
 int32_t qsvd_decode_default_splits(int32_t b, int64_t L, int32_t r, int32_t heads, int32_t d,
                                    qsvd_dtype_t c_dtype);

@@ -16,7 +16,9 @@ __all__ = [
     "F32", "BF16", "I8", "I4", "QsvdError", "lib", "library_path",
     "qsvd_quantize_latent", "qsvd_project", "qsvd_pack_weight",
     "qsvd_decode_workspace_bytes", "qsvd_decode_default_splits", "qsvd_decode_attn",
-    "qsvd_decode_explicit_workspace_bytes", "qsvd_decode_attn_explicit", "qsvd_status_string", "qsvd_last_error", "timing", "EXPORTED",
+    "qsvd_decode_explicit_workspace_bytes", "qsvd_decode_attn_explicit",
+    "qsvd_decode_headwise_workspace_bytes", "qsvd_decode_attn_headwise",
+    "qsvd_status_string", "qsvd_last_error", "timing", "EXPORTED",
 ]
 
 F32, BF16, I8, I4 = 0, 1, 2, 3
@@ -27,7 +29,8 @@ library_path = os.path.join(_PKG, "libqsvd.so")
 EXPORTED = (
     "qsvd_quantize_latent", "qsvd_project", "qsvd_pack_weight", "qsvd_decode_workspace_bytes",
     "qsvd_decode_attn", "qsvd_decode_default_splits", "qsvd_decode_explicit_workspace_bytes",
-    "qsvd_decode_attn_explicit", "qsvd_status_string", "qsvd_last_error",
+    "qsvd_decode_attn_explicit", "qsvd_decode_headwise_workspace_bytes",
+    "qsvd_decode_attn_headwise", "qsvd_status_string", "qsvd_last_error",
     "qsvd_timing_begin", "qsvd_timing_end",
 )
 
@@ -68,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.qsvd_decode_explicit_workspace_bytes.restype = sz
     L.qsvd_decode_attn_explicit.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
                                             ctypes.c_float, f32p, f32p, vp, i32, vp, sz, vp]
+    L.qsvd_decode_headwise_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    L.qsvd_decode_headwise_workspace_bytes.restype = sz
+    L.qsvd_decode_attn_headwise.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
+                                            i32, ctypes.c_float, f32p, f32p, i32, vp, i32, vp, sz, vp]
     L.qsvd_status_string.argtypes = [i32]
     L.qsvd_status_string.restype = ctypes.c_char_p
     L.qsvd_last_error.argtypes = []
@@ -75,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.qsvd_timing_begin.argtypes = [i32]
     L.qsvd_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
     for name in ("qsvd_quantize_latent", "qsvd_project", "qsvd_pack_weight", "qsvd_decode_attn",
-                 "qsvd_decode_attn_explicit", "qsvd_timing_begin", "qsvd_timing_end", "qsvd_decode_default_splits"):
+                 "qsvd_decode_attn_explicit", "qsvd_decode_attn_headwise", "qsvd_timing_begin", "qsvd_timing_end", "qsvd_decode_default_splits"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -162,6 +169,23 @@ def qsvd_decode_attn_explicit(q, q_dtype, C, c_dtype, Wk_packed, Wv_packed, wu_d
                                            _ptr(O), o_dtype, _ptr(workspace), workspace_bytes,
                                            _stream(stream)),
            "qsvd_decode_attn_explicit")
+
+
+def qsvd_decode_headwise_workspace_bytes(b, L, heads, d, rk, rv, splits=0) -> int:
+    return int(lib().qsvd_decode_headwise_workspace_bytes(b, L, heads, d, rk, rv, splits))
+
+
+def qsvd_decode_attn_headwise(q, q_dtype, C, c_dtype, BK_t, BV, b_dtype, b, L, heads, d, rk, rv,
+                              softmax_scale, rope_cos, rope_sin, splits, O, o_dtype, workspace,
+                              workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qsvd_decode_attn_headwise(_ptr(q), q_dtype, _ptr(C), c_dtype, _ptr(BK_t), _ptr(BV),
+                                           b_dtype, b, L, heads, d, rk, rv, float(softmax_scale),
+                                           _ptr(rope_cos), _ptr(rope_sin), splits, _ptr(O),
+                                           o_dtype, _ptr(workspace), workspace_bytes,
+                                           _stream(stream)),
+           "qsvd_decode_attn_headwise")
 
 
 class timing:

@@ -288,6 +288,80 @@ qsvd_status_t qsvd_decode_attn_explicit(const void *q, qsvd_dtype_t q_dtype, con
                        "decode_attn_explicit");
 }
 
+static qsvd_status_t validate_headwise_shape(int32_t b, int64_t L, int32_t heads, int32_t d,
+                                             int32_t rk, int32_t rv, int32_t splits) {
+  if (b < 1) return fail(QSVD_ERR_INVALID, "decode_headwise: b = %d < 1", b);
+  if (L < 1) return fail(QSVD_ERR_INVALID, "decode_headwise: L = %lld < 1", (long long)L);
+  if (heads < 1 || heads > 256)
+    return fail(QSVD_ERR_INVALID, "decode_headwise: heads = %d (1..256)", heads);
+  if (d != 128) return fail(QSVD_ERR_UNSUPPORTED, "decode_headwise: d = %d (128)", d);
+  if (rk < 32 || rk > 128 || rk % 32 != 0 || rv < 32 || rv > 128 || rv % 32 != 0)
+    return fail(QSVD_ERR_UNSUPPORTED, "decode_headwise: rk = %d, rv = %d (each 32, 64, 96 or 128)",
+                rk, rv);
+  if (splits < 0 || splits > 1024)
+    return fail(QSVD_ERR_INVALID, "decode_headwise: splits = %d (0..1024)", splits);
+  if (static_cast<int64_t>(b) * L > (int64_t(1) << 36))
+    return fail(QSVD_ERR_INVALID, "decode_headwise: b * L too large");
+  const int64_t grid = static_cast<int64_t>(b) * qsvd::headwise_splits(b, L, heads, splits) *
+                       ((heads + 3) / 4);
+  if (grid >= (int64_t(1) << 31)) return fail(QSVD_ERR_INVALID, "decode_headwise: b too large");
+  return QSVD_OK;
+}
+
+size_t qsvd_decode_headwise_workspace_bytes(int32_t b, int64_t L, int32_t heads, int32_t d,
+                                            int32_t rk, int32_t rv, int32_t splits) {
+  if (validate_headwise_shape(b, L, heads, d, rk, rv, splits) != QSVD_OK) return 0;
+  return qsvd::headwise_workspace_bytes(b, L, heads, rv, splits);
+}
+
+qsvd_status_t qsvd_decode_attn_headwise(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                        qsvd_dtype_t c_dtype, const void *BK_t, const void *BV,
+                                        qsvd_dtype_t b_dtype, int32_t b, int64_t L, int32_t heads,
+                                        int32_t d, int32_t rk, int32_t rv, float softmax_scale,
+                                        const float *rope_cos, const float *rope_sin,
+                                        int32_t splits, void *O, qsvd_dtype_t o_dtype,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *hip_stream) {
+  qsvd_status_t st = validate_headwise_shape(b, L, heads, d, rk, rv, splits);
+  if (st != QSVD_OK) return st;
+  if (q_dtype != QSVD_BF16 || c_dtype != QSVD_BF16 || b_dtype != QSVD_BF16)
+    return fail(QSVD_ERR_UNSUPPORTED, "decode_headwise: q, C and B_K / B_V must be BF16");
+  if (o_dtype != QSVD_BF16 && o_dtype != QSVD_F32)
+    return fail(QSVD_ERR_INVALID, "decode_headwise: o_dtype %s", dtype_name(o_dtype));
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
+    return fail(QSVD_ERR_INVALID, "decode_headwise: softmax_scale must be positive and finite");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(QSVD_ERR_INVALID, "decode_headwise: rope_cos and rope_sin go together");
+  if (!q || !C || !BK_t || !BV || !O) return fail(QSVD_ERR_INVALID, "decode_headwise: NULL pointer");
+  if (!aligned16(q) || !aligned16(C) || !aligned16(BK_t) || !aligned16(BV) || !aligned16(O) ||
+      (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
+      (workspace && !aligned16(workspace)))
+    return fail(QSVD_ERR_INVALID, "decode_headwise: misaligned pointer");
+  const size_t need = qsvd::headwise_workspace_bytes(b, L, heads, rv, splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(QSVD_ERR_WORKSPACE, "decode_headwise: workspace %zu bytes, need %zu",
+                workspace_bytes, need);
+  qsvd::HeadwiseArgs a{};
+  a.q = q;
+  a.C = C;
+  a.BK_t = BK_t;
+  a.BV = BV;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.b = b;
+  a.L = L;
+  a.heads = heads;
+  a.rk = rk;
+  a.rv = rv;
+  a.splits = splits;
+  a.softmax_scale = softmax_scale;
+  a.O = O;
+  a.o_dtype = o_dtype;
+  a.workspace = workspace;
+  return device_status(qsvd::launch_decode_headwise(a, static_cast<hipStream_t>(hip_stream)),
+                       "decode_attn_headwise");
+}
+
 qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *C,
                                qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
                                const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,

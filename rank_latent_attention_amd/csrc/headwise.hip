@@ -1,0 +1,417 @@
+// Decode over per-head latents (WSVD), keys rebuilt on chip, optional RoPE (gfx950).
+//
+// WSVD digest, "Method, 3.1": every head has its own low-rank factors,
+// W_Kh = A_Kh B_Kh, and caches its own latent C_Kh = X A_Kh (r values per
+// token and head instead of one shared R-wide latent), and the same for V.
+// "Method, 3.4": the fused flash-decoding kernel streams C_Kh tiles, rebuilds
+// K_{h,t} = C_{Kh,t} B_Kh in registers, applies RoPE, contracts with q_h, and
+// fuses B_Vh into the output side instead of rebuilding V.
+//
+// Cache layout: C[b][L][heads][rk + rv] bf16, each head's key latent followed
+// by its value latent, so one token's row holds every head.  Weights: B_Kh
+// transposed, BK_t[heads][128][rk] (contiguous along the latent), and
+// BV[heads][rv][128].
+//
+// headwise_stream_kernel: workgroup (sequence, split, 4 heads), one wavefront
+// per head and nothing shared between wavefronts.  A wavefront keeps its head's
+// B_Kh fragments in registers for the whole split and, per 32-token tile:
+//   1. 16-byte buffer loads of the tile's key and value latents of its head,
+//      one tile ahead (rows past L read as zero and are masked);
+//   2. K (32 x 128) = C_K (32 x rk) B_Kh with v_mfma_f32_16x16x32_bf16, the
+//      latent rows straight from the load registers as the A operand;
+//   3. RoPE: dimension i pairs with i + 64, both in the same lane (column
+//      blocks nb and nb + 4), rotated with the caller's cos / sin tables;
+//   4. scores (dot with the rotated, pre-scaled query: 16-lane DPP sums),
+//      the online softmax of the split (log2 units);
+//   5. O~ += p^T C_V: each lane accumulates its own tokens' value columns;
+//      p moves from the score lanes to the value lanes through 128 bytes of
+//      the wavefront's LDS.
+// The lanes' O~ shares are summed once per split; (m, l, O~) go to the
+// workspace.  headwise_merge_kernel combines the splits by their log-sum-exp
+// weights and applies B_Vh.
+#include "device_common.h"
+#include "qsvd_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace qsvd {
+namespace {
+
+constexpr float kLog2eH = 1.4426950408889634f;
+constexpr int kHd = 128;         // head dimension of this path
+constexpr int kHT = 32;          // tokens per tile
+constexpr int kHeadsPerWg = 4;   // one wavefront per head
+constexpr int kHwCUs = 256;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// sum over each aligned group of 16 lanes (xor 1, xor 2, mirror in 8, mirror in 16)
+__device__ __forceinline__ float sum16(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  v = dpp_add<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t hw_rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(n), 0x00020000);
+}
+
+struct HeadwiseParams {
+  const uint16_t *q;
+  const uint8_t *C;
+  const uint16_t *BK_t;
+  const float *rope_cos, *rope_sin;
+  float *part;
+  int64_t L;
+  int heads, S;
+  float scale_log2;
+};
+
+// Registers a wavefront needs (B_Kh fragments, two tile buffers, K accumulators,
+// O~ shares, the cos / sin of a tile, addresses): two wavefronts per SIMD when
+// they fit in 256, else one with up to 512.
+template <int KBK, int KBV, bool ROPE>
+constexpr int hw_occupancy() {
+  return 32 * KBK + 16 * (KBK + KBV) + 8 * KBV + 104 + (ROPE ? 64 : 0) <= 256 ? 2 : 1;
+}
+
+// Head dimension held by lane li in column block nb of K: lane li owns
+// dimensions 4 li .. 4 li + 3 (blocks 0-3) and 64 + 4 li .. 64 + 4 li + 3
+// (blocks 4-7), so a RoPE pair (i, i + 64) sits in one lane and the lane's
+// cos / sin values of a position are one 16-byte load.
+__device__ __forceinline__ int hw_dim(int nb, int li) { return (nb >> 2) * 64 + 4 * li + (nb & 3); }
+
+template <int KBK, int KBV, bool ROPE>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(hw_occupancy<KBK, KBV, ROPE>(), hw_occupancy<KBK, KBV, ROPE>())))
+void headwise_stream_kernel(HeadwiseParams p) {
+  constexpr int RK = 32 * KBK, RV = 32 * KBV, NC = KBK + KBV;
+  constexpr int NB = kHd / 16;   // 16-column blocks of K
+  __shared__ float pbuf[kHeadsPerWg][kHT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int G = (p.heads + kHeadsPerWg - 1) / kHeadsPerWg;
+  int task;
+  {
+    const int total = gridDim.x, id = blockIdx.x;
+    const int per = total / 8, rem = total % 8, xcd = id % 8, local = id / 8;
+    task = xcd * per + min(xcd, rem) + local;
+  }
+  const int grp = task % G;
+  const int split = (task / G) % p.S;
+  const int64_t seq = task / (G * p.S);
+  const int h = grp * kHeadsPerWg + wave;
+  if (h >= p.heads) return;   // wavefronts share nothing: no barrier anywhere
+
+  const int64_t L = p.L;
+  const int64_t tiles_all = (L + kHT - 1) / kHT;
+  const int ntiles = split < tiles_all ? static_cast<int>((tiles_all - split + p.S - 1) / p.S) : 0;
+  const int64_t row_bytes = static_cast<int64_t>(p.heads) * (RK + RV) * 2;
+  const uint32_t head_off = static_cast<uint32_t>(h * (RK + RV) * 2);
+  auto tile_t0 = [&](int it) { return (static_cast<int64_t>(split) + static_cast<int64_t>(it) * p.S) * kHT; };
+
+  // tile registers: [buffer][16-token half][chunk]; chunk c < KBK holds key
+  // columns 32 c + 8 lg .. +8, chunk KBK + v value columns 32 v + 8 lg .. +8, of
+  // token 16 half + li
+  u32x4 tl[2][2][NC];
+  auto load_tile = [&](auto BUF, int it) {
+    constexpr int bf = decltype(BUF)::value;
+    const int64_t t0 = tile_t0(it);
+    const __amdgpu_buffer_rsrc_t rc = hw_rsrc(p.C + (seq * L + t0) * row_bytes, (L - t0) * row_bytes);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t ro = static_cast<uint32_t>((16 * hf + li) * row_bytes) + head_off;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int col = c < KBK ? 32 * c + 8 * lg : RK + 32 * (c - KBK) + 8 * lg;
+        tl[bf][hf][c] = __builtin_amdgcn_raw_buffer_load_b128(rc, ro + col * 2, 0, 0);
+      }
+    }
+  };
+  if (ntiles > 0) load_tile(std::integral_constant<int, 0>{}, 0);
+
+  // B_Kh fragments (B operand: column hw_dim(nb, li), latent rows 32 kb + 8 lg .. +8)
+  bf16x8 bk[NB][KBK];
+  const uint16_t *bkh = p.BK_t + static_cast<int64_t>(h) * kHd * RK;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb)
+      bk[nb][kb] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(bkh + hw_dim(nb, li) * RK + 32 * kb + 8 * lg));
+
+  // rotated query scaled by softmax_scale log2(e), this lane's dimensions
+  float qr[NB];
+  {
+    const uint16_t *qh = p.q + (seq * p.heads + h) * kHd;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * li + j;
+      const float x0 = bf16_to_f32(qh[i]), x1 = bf16_to_f32(qh[i + kHd / 2]);
+      float y0 = x0, y1 = x1;
+      if constexpr (ROPE) {
+        const float c = p.rope_cos[(L - 1) * (kHd / 2) + i], s = p.rope_sin[(L - 1) * (kHd / 2) + i];
+        y0 = x0 * c - x1 * s;
+        y1 = x1 * c + x0 * s;
+      }
+      qr[j] = y0 * p.scale_log2;
+      qr[j + 4] = y1 * p.scale_log2;
+    }
+  }
+
+  float m = -INFINITY, l = 0.f;
+  float ov[KBV][8];   // this lane's tokens' value columns 32 v + 8 lg + c, summed over tiles
+#pragma unroll
+  for (int v = 0; v < KBV; ++v)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ov[v][c] = 0.f;
+
+  auto body = [&](auto BUF, int it) {
+    constexpr int bf = decltype(BUF)::value;
+    const int64_t t0 = tile_t0(it);
+    // cos / sin of this lane's tokens 16 hf + 4 lg + e (clamped past L; masked below)
+    f32x4 rc[2][4], rs[2][4];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t pos = t0 + 16 * hf + 4 * lg + e;
+          const int64_t off = (pos < L ? pos : L - 1) * (kHd / 2) + 4 * li;
+          rc[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_cos + off);
+          rs[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_sin + off);
+        }
+    }
+    // the next tile (a repeat of the last one past the end, never used)
+    load_tile(std::integral_constant<int, 1 - bf>{}, min(it + 1, ntiles - 1));
+
+    float sc[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      // K = C_K B_Kh; element e of lane: token 16 hf + 4 lg + e, dimension hw_dim(nb, li)
+      f32x4 kacc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KBK; ++kb)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tl[bf][hf][kb]), bk[nb][kb], a,
+                                                      0, 0, 0);
+        kacc[nb] = a;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s = 0.f;
+        if constexpr (ROPE) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float c = rc[hf][e][j], sn = rs[hf][e][j];
+            const float k0 = kacc[j][e], k1 = kacc[j + 4][e];
+            s = fmaf(k0 * c - k1 * sn, qr[j], s);
+            s = fmaf(k1 * c + k0 * sn, qr[j + 4], s);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) s = fmaf(kacc[nb][e], qr[nb], s);
+        }
+        s = sum16(s);
+        sc[hf][e] = t0 + 16 * hf + 4 * lg + e < L ? s : -INFINITY;
+      }
+    }
+
+    // ---- online softmax over the 32 tokens (each score sits in 16 lanes)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[hf][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m, mx);   // finite: the first token of a tile is < L
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sc[hf][e] - m_new);   // 0 for masked tokens
+        sc[hf][e] = pe;
+        psum += pe;
+      }
+    psum += __shfl_xor(psum, 16, kWave);
+    psum += __shfl_xor(psum, 32, kWave);
+    l = fmaf(l, alpha, psum);
+    m = m_new;
+
+    // ---- p to the value lanes: lane li owns tokens li and 16 + li
+    if (li == 0) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pbuf[wave][16 * hf + 4 * lg + e] = sc[hf][e];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float p0 = pbuf[wave][li], p1 = pbuf[wave][16 + li];
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- O~ = alpha O~ + p^T C_V over this lane's two tokens
+#pragma unroll
+    for (int v = 0; v < KBV; ++v) {
+      const u32x4 w0 = tl[bf][0][KBK + v], w1 = tl[bf][1][KBK + v];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float lo = fmaf(p0, __uint_as_float(w0[c] << 16), ov[v][2 * c] * alpha);
+        float hi = fmaf(p0, __uint_as_float(w0[c] & 0xFFFF0000u), ov[v][2 * c + 1] * alpha);
+        ov[v][2 * c] = fmaf(p1, __uint_as_float(w1[c] << 16), lo);
+        ov[v][2 * c + 1] = fmaf(p1, __uint_as_float(w1[c] & 0xFFFF0000u), hi);
+      }
+    }
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    body(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntiles) body(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  // ---- the split's partial state: O~ summed over the 16 lanes (tokens) of each group
+  float *dst = p.part + ((seq * p.S + split) * p.heads + h) * (RV + 4);
+#pragma unroll
+  for (int v = 0; v < KBV; ++v)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float t = sum16(ov[v][c]);
+      if (li == 0) dst[4 + 32 * v + 8 * lg + c] = t;
+    }
+  if (lane == 0) {
+    dst[0] = m;
+    dst[1] = l;
+    dst[2] = 0.f;
+    dst[3] = 0.f;
+  }
+}
+
+// One wavefront per (sequence, head): O~ = sum_s 2^(m_s - M) O~_s / sum_s 2^(m_s - M) l_s,
+// then O = O~ B_Vh.
+template <typename OT>
+__global__ __launch_bounds__(256) void headwise_merge_kernel(const float *__restrict__ part,
+                                                             const uint16_t *__restrict__ BV,
+                                                             OT *__restrict__ O, int b, int heads,
+                                                             int S, int rv) {
+  __shared__ float om[4][kHd];
+  const int wl = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + wl;
+  if (w >= b * heads) return;   // uniform per wavefront; barriers below are wave-local
+  const int seq = w / heads, h = w % heads;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part[((static_cast<int64_t>(seq) * S + s) * heads + h) * (rv + 4)]);
+  float den = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float *src = part + ((static_cast<int64_t>(seq) * S + s) * heads + h) * (rv + 4);
+    const float wgt = src[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(src[0] - M);
+    den = fmaf(wgt, src[1], den);
+    if (lane < rv) o0 = fmaf(wgt, src[4 + lane], o0);
+    if (lane + 64 < rv) o1 = fmaf(wgt, src[4 + 64 + lane], o1);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  om[wl][lane] = o0 * inv;
+  om[wl][lane + 64] = o1 * inv;
+  __builtin_amdgcn_wave_barrier();
+  const uint16_t *bv = BV + static_cast<int64_t>(h) * rv * kHd;
+  float a0 = 0.f, a1 = 0.f;
+  for (int c = 0; c < rv; ++c) {
+    const float oc = om[wl][c];
+    a0 = fmaf(oc, bf16_to_f32(bv[c * kHd + lane]), a0);
+    a1 = fmaf(oc, bf16_to_f32(bv[c * kHd + 64 + lane]), a1);
+  }
+  OT *out = O + (static_cast<int64_t>(seq) * heads + h) * kHd;
+  if constexpr (sizeof(OT) == 2) {
+    out[lane] = f32_to_bf16(a0);
+    out[64 + lane] = f32_to_bf16(a1);
+  } else {
+    out[lane] = a0;
+    out[64 + lane] = a1;
+  }
+}
+
+template <int KBK, int KBV>
+hipError_t launch_hw_t(const HeadwiseParams &hp, bool rope, int grid, hipStream_t s) {
+  if (rope)
+    headwise_stream_kernel<KBK, KBV, true><<<dim3(grid), dim3(256), 0, s>>>(hp);
+  else
+    headwise_stream_kernel<KBK, KBV, false><<<dim3(grid), dim3(256), 0, s>>>(hp);
+  return hipGetLastError();
+}
+
+template <int KBK>
+hipError_t launch_hw_k(const HeadwiseParams &hp, int rv, bool rope, int grid, hipStream_t s) {
+  switch (rv) {
+    case 32: return launch_hw_t<KBK, 1>(hp, rope, grid, s);
+    case 64: return launch_hw_t<KBK, 2>(hp, rope, grid, s);
+    case 96: return launch_hw_t<KBK, 3>(hp, rope, grid, s);
+    default: return launch_hw_t<KBK, 4>(hp, rope, grid, s);
+  }
+}
+
+}  // namespace
+
+int headwise_splits(int b, int64_t L, int heads, int splits) {
+  const int64_t tiles = (L + kHT - 1) / kHT;
+  const int64_t groups = static_cast<int64_t>(b) * ((heads + kHeadsPerWg - 1) / kHeadsPerWg);
+  int64_t S = splits > 0 ? splits : std::max<int64_t>(1, kHwCUs * 2 / std::max<int64_t>(groups, 1));
+  S = std::min<int64_t>(std::min<int64_t>(S, tiles), 1024);
+  return static_cast<int>(std::max<int64_t>(S, 1));
+}
+
+size_t headwise_workspace_bytes(int b, int64_t L, int heads, int rv, int splits) {
+  const int S = headwise_splits(b, L, heads, splits);
+  return static_cast<size_t>(b) * S * heads * (rv + 4) * sizeof(float);
+}
+
+hipError_t launch_decode_headwise(const HeadwiseArgs &a, hipStream_t s) {
+  const int S = headwise_splits(a.b, a.L, a.heads, a.splits);
+  const int G = (a.heads + kHeadsPerWg - 1) / kHeadsPerWg;
+  const int grid = a.b * S * G;
+  HeadwiseParams hp{};
+  hp.q = static_cast<const uint16_t *>(a.q);
+  hp.C = static_cast<const uint8_t *>(a.C);
+  hp.BK_t = static_cast<const uint16_t *>(a.BK_t);
+  hp.rope_cos = a.rope_cos;
+  hp.rope_sin = a.rope_sin;
+  hp.part = static_cast<float *>(a.workspace);
+  hp.L = a.L;
+  hp.heads = a.heads;
+  hp.S = S;
+  hp.scale_log2 = a.softmax_scale * kLog2eH;
+  hipError_t e;
+  {
+    LaunchTimer t("headwise_stream", s);
+    const bool rope = a.rope_cos != nullptr;
+    switch (a.rk) {
+      case 32: e = launch_hw_k<1>(hp, a.rv, rope, grid, s); break;
+      case 64: e = launch_hw_k<2>(hp, a.rv, rope, grid, s); break;
+      case 96: e = launch_hw_k<3>(hp, a.rv, rope, grid, s); break;
+      default: e = launch_hw_k<4>(hp, a.rv, rope, grid, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  LaunchTimer t("headwise_merge", s);
+  const dim3 mgrid(static_cast<unsigned>((a.b * a.heads + 3) / 4)), block(256);
+  if (a.o_dtype == QSVD_BF16)
+    headwise_merge_kernel<uint16_t><<<mgrid, block, 0, s>>>(hp.part, static_cast<const uint16_t *>(a.BV),
+                                                            static_cast<uint16_t *>(a.O), a.b, a.heads, S, a.rv);
+  else
+    headwise_merge_kernel<float><<<mgrid, block, 0, s>>>(hp.part, static_cast<const uint16_t *>(a.BV),
+                                                         static_cast<float *>(a.O), a.b, a.heads, S, a.rv);
+  return hipGetLastError();
+}
+
+}  // namespace qsvd

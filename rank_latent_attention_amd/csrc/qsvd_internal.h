@@ -63,6 +63,26 @@ struct ExplicitArgs {
 size_t explicit_workspace_bytes(int b, int64_t L, int heads);
 hipError_t launch_decode_explicit(const ExplicitArgs &a, hipStream_t s);
 
+struct HeadwiseArgs {
+  const void *q;        // [b][heads][128] bf16
+  const void *C;        // [b][L][heads][rk + rv] bf16
+  const void *BK_t;     // [heads][128][rk] bf16 (B_Kh transposed)
+  const void *BV;       // [heads][rv][128] bf16
+  const float *rope_cos, *rope_sin;   // [>= L][64] each, or both NULL
+  int b;
+  int64_t L;
+  int heads, rk, rv, splits;
+  float softmax_scale;
+  void *O;
+  int o_dtype;
+  void *workspace;
+};
+
+// Splits per sequence of a per-head-latent decode (splits = 0: default).
+int headwise_splits(int b, int64_t L, int heads, int splits);
+size_t headwise_workspace_bytes(int b, int64_t L, int heads, int rv, int splits);
+hipError_t launch_decode_headwise(const HeadwiseArgs &a, hipStream_t s);
+
 struct DecodeArgs {
   const void *q;
   int q_dtype;

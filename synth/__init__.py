@@ -464,8 +464,10 @@ def headwise_case(b: int, L: int, heads: int, d: int, rk: int, rv: int, *, p: fl
         z[:, out_ch] *= 8.0
         ck = z[:, : heads * rk] * colk
         cv = z[:, heads * rk:] * colv
-        Cs.append(np.concatenate([ck.reshape(L, heads, rk), cv.reshape(L, heads, rv)], axis=2))
+        Cs.append(to_bf16_bits(np.concatenate([ck.reshape(L, heads, rk), cv.reshape(L, heads, rv)],
+                                              axis=2)))
+        del z, ck, cv
         qs.append(rng(seed, _XNEW, s).standard_normal((heads, d)) * 2.0)
-    return HeadwiseCase(len(qs), L, heads, d, rk, rv, to_bf16_bits(np.stack(qs)),
-                        to_bf16_bits(np.stack(Cs)), to_bf16_bits(np.ascontiguousarray(BK.transpose(0, 2, 1))),
+    return HeadwiseCase(len(qs), L, heads, d, rk, rv, to_bf16_bits(np.stack(qs)), np.stack(Cs),
+                        to_bf16_bits(np.ascontiguousarray(BK.transpose(0, 2, 1))),
                         to_bf16_bits(BV), 1.0 / math.sqrt(d))

@@ -179,3 +179,40 @@ def test_decode_explicit_validation():
     assert need == 2 * 2 * 4 * 132 * 4
     assert st_exp(wsb=need - 1) == -3
     assert q.qsvd_decode_explicit_workspace_bytes(2, 300, 256, 4, 64) == 0
+
+
+def st_hw(**kw):
+    a = dict(q_=FAKE, qdt=q.BF16, C=FAKE, cdt=q.BF16, BK=FAKE, BV=FAKE, bdt=q.BF16, b=2, L=300,
+             heads=6, d=128, rk=64, rv=32, scale=0.088, rc=None, rs=None, splits=0, O=FAKE,
+             odt=q.BF16, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return q.lib().qsvd_decode_attn_headwise(a["q_"], a["qdt"], a["C"], a["cdt"], a["BK"], a["BV"],
+                                             a["bdt"], a["b"], a["L"], a["heads"], a["d"], a["rk"],
+                                             a["rv"], a["scale"], a["rc"], a["rs"], a["splits"],
+                                             a["O"], a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_headwise_validation():
+    assert st_hw(b=0) == -1
+    assert st_hw(L=0) == -1
+    assert st_hw(heads=0) == -1
+    assert st_hw(heads=257) == -1
+    assert st_hw(d=64) == -2
+    for rk, rv in ((16, 64), (48, 64), (160, 64), (64, 0), (64, 100)):
+        assert st_hw(rk=rk, rv=rv) == -2, (rk, rv)
+    assert st_hw(cdt=q.I8) == -2
+    assert st_hw(bdt=q.F32) == -2
+    assert st_hw(odt=q.I4) == -1
+    assert st_hw(rs=FAKE) == -1                   # the two tables go together
+    assert st_hw(scale=0.0) == -1
+    assert st_hw(splits=-1) == -1
+    assert st_hw(splits=1025) == -1
+    assert st_hw(BK=None) == -1
+    assert st_hw(O=ctypes.c_void_p((1 << 20) + 8)) == -1
+    # default splits: 2 x 256 / (b x ceil(heads / 4)) = 128, clipped to the 10 tiles of L = 300
+    need = q.qsvd_decode_headwise_workspace_bytes(2, 300, 6, 128, 64, 32, 0)
+    assert need == 2 * 10 * 6 * (32 + 4) * 4
+    assert q.qsvd_decode_headwise_workspace_bytes(2, 300, 6, 128, 64, 32, 3) == 2 * 3 * 6 * 36 * 4
+    assert q.qsvd_decode_headwise_workspace_bytes(2, 300, 6, 64, 64, 32, 0) == 0
+    assert st_hw(wsb=need - 1) == -3
+    assert st_hw(ws=None) == -3
