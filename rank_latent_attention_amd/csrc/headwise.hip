@@ -74,13 +74,19 @@ struct HeadwiseParams {
   float scale_log2;
 };
 
-// Registers a wavefront needs (B_Kh fragments, two tile buffers, K accumulators,
-// O~ shares, the cos / sin of a tile, addresses): two wavefronts per SIMD when
-// they fit in 256, else one with up to 512.
+// Launch shape of one (rk, rv, RoPE) instance.  Registers a wavefront needs
+// (B_Kh fragments, two tile buffers, K accumulators, O~ shares, the rotated
+// query, addresses) decide between two wavefronts per SIMD (<= 256) and one
+// (<= 512).  The in-tile RoPE rows (64 values a lane) sit in LDS when that
+// buys the second wavefront, else in registers; a lone wavefront keeps two
+// tiles in flight (three buffers) when its registers allow.
 template <int KBK, int KBV, bool ROPE>
-constexpr int hw_occupancy() {
-  return 32 * KBK + 16 * (KBK + KBV) + 8 * KBV + 104 + (ROPE ? 64 : 0) <= 256 ? 2 : 1;
-}
+struct HwShape {
+  static constexpr int kBase = 32 * KBK + 16 * (KBK + KBV) + 8 * KBV + 104;
+  static constexpr bool kRowsInLds = ROPE && kBase + 8 <= 256;
+  static constexpr int kOcc = kBase + (ROPE ? (kRowsInLds ? 8 : 64) : 0) <= 256 ? 2 : 1;
+  static constexpr int kBufs = kOcc == 1 && kBase + (ROPE ? 64 : 0) + 8 * (KBK + KBV) <= 440 ? 3 : 2;
+};
 
 // Head dimension held by lane li in column block nb of K: lane li owns
 // dimensions 4 li .. 4 li + 3 (blocks 0-3) and 64 + 4 li .. 64 + 4 li + 3
@@ -90,11 +96,15 @@ __device__ __forceinline__ int hw_dim(int nb, int li) { return (nb >> 2) * 64 + 
 
 template <int KBK, int KBV, bool ROPE>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(hw_occupancy<KBK, KBV, ROPE>(), hw_occupancy<KBK, KBV, ROPE>())))
+__attribute__((amdgpu_waves_per_eu(HwShape<KBK, KBV, ROPE>::kOcc, HwShape<KBK, KBV, ROPE>::kOcc)))
 void headwise_stream_kernel(HeadwiseParams p) {
   constexpr int RK = 32 * KBK, RV = 32 * KBV, NC = KBK + KBV;
   constexpr int NB = kHd / 16;   // 16-column blocks of K
+  constexpr int NBUF = HwShape<KBK, KBV, ROPE>::kBufs;
+  constexpr bool RT_LDS = HwShape<KBK, KBV, ROPE>::kRowsInLds;
   __shared__ float pbuf[kHeadsPerWg][kHT];
+  // RoPE rows 0 .. 31 (cos, sin), the in-tile rotations, shared by the heads
+  __shared__ f32x4 rt[RT_LDS ? 2 : 1][RT_LDS ? kHT : 1][16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -110,7 +120,15 @@ void headwise_stream_kernel(HeadwiseParams p) {
   const int split = (task / G) % p.S;
   const int64_t seq = task / (G * p.S);
   const int h = grp * kHeadsPerWg + wave;
-  if (h >= p.heads) return;   // wavefronts share nothing: no barrier anywhere
+  if constexpr (RT_LDS) {
+    for (int i = threadIdx.x; i < 2 * kHT * 16; i += blockDim.x) {
+      const int tb = i / (kHT * 16), row = (i / 16) % kHT, c4 = i % 16;
+      const int64_t r = row < p.L ? row : p.L - 1;   // rows past L: never used unmasked
+      rt[tb][row][c4] = *reinterpret_cast<const f32x4 *>((tb ? p.rope_sin : p.rope_cos) + r * (kHd / 2) + 4 * c4);
+    }
+    __syncthreads();   // the only barrier: before any wavefront leaves
+  }
+  if (h >= p.heads) return;   // past this point the wavefronts share nothing
 
   const int64_t L = p.L;
   const int64_t tiles_all = (L + kHT - 1) / kHT;
@@ -122,7 +140,7 @@ void headwise_stream_kernel(HeadwiseParams p) {
   // tile registers: [buffer][16-token half][chunk]; chunk c < KBK holds key
   // columns 32 c + 8 lg .. +8, chunk KBK + v value columns 32 v + 8 lg .. +8, of
   // token 16 half + li
-  u32x4 tl[2][2][NC];
+  u32x4 tl[NBUF][2][NC];
   auto load_tile = [&](auto BUF, int it) {
     constexpr int bf = decltype(BUF)::value;
     const int64_t t0 = tile_t0(it);
@@ -137,7 +155,10 @@ void headwise_stream_kernel(HeadwiseParams p) {
       }
     }
   };
-  if (ntiles > 0) load_tile(std::integral_constant<int, 0>{}, 0);
+  if (ntiles > 0) {
+    load_tile(std::integral_constant<int, 0>{}, 0);
+    if constexpr (NBUF == 3) load_tile(std::integral_constant<int, 1>{}, min(1, ntiles - 1));
+  }
 
   // B_Kh fragments (B operand: column hw_dim(nb, li), latent rows 32 kb + 8 lg .. +8)
   bf16x8 bk[NB][KBK];
@@ -160,12 +181,25 @@ void headwise_stream_kernel(HeadwiseParams p) {
       float y0 = x0, y1 = x1;
       if constexpr (ROPE) {
         const float c = p.rope_cos[(L - 1) * (kHd / 2) + i], s = p.rope_sin[(L - 1) * (kHd / 2) + i];
-        y0 = x0 * c - x1 * s;
-        y1 = x1 * c + x0 * s;
+        y0 = fmaf(x0, c, -(x1 * s));
+        y1 = fmaf(x1, c, x0 * s);
       }
       qr[j] = y0 * p.scale_log2;
       qr[j + 4] = y1 * p.scale_log2;
     }
+  }
+  // in-tile RoPE rows in registers: offset o = 16 hf + 4 lg + e of this lane's tokens
+  f32x4 oc[2][4], os[2][4];
+  if constexpr (ROPE && !RT_LDS) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t o = 16 * hf + 4 * lg + e;
+        const int64_t off = (o < L ? o : L - 1) * (kHd / 2) + 4 * li;
+        oc[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_cos + off);
+        os[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_sin + off);
+      }
   }
 
   float m = -INFINITY, l = 0.f;
@@ -178,21 +212,23 @@ void headwise_stream_kernel(HeadwiseParams p) {
   auto body = [&](auto BUF, int it) {
     constexpr int bf = decltype(BUF)::value;
     const int64_t t0 = tile_t0(it);
-    // cos / sin of this lane's tokens 16 hf + 4 lg + e (clamped past L; masked below)
-    f32x4 rc[2][4], rs[2][4];
+    // RoPE: rot(K_t, t) . rot(q, L - 1) = K_t . R(-o) y with y = R(-t0) rot(q, L - 1)
+    // for token t = t0 + o; rotations by position compose (angles are t theta_i),
+    // so a tile reads table row t0 besides the in-tile rows 0 .. 31 held all along
+    float y0[4], y1[4];
     if constexpr (ROPE) {
+      const int64_t off = t0 * (kHd / 2) + 4 * li;
+      const f32x4 c0 = *reinterpret_cast<const f32x4 *>(p.rope_cos + off);
+      const f32x4 s0 = *reinterpret_cast<const f32x4 *>(p.rope_sin + off);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t pos = t0 + 16 * hf + 4 * lg + e;
-          const int64_t off = (pos < L ? pos : L - 1) * (kHd / 2) + 4 * li;
-          rc[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_cos + off);
-          rs[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_sin + off);
-        }
+      for (int j = 0; j < 4; ++j) {
+        y0[j] = fmaf(qr[j], c0[j], qr[j + 4] * s0[j]);
+        y1[j] = fmaf(qr[j + 4], c0[j], -(qr[j] * s0[j]));
+      }
     }
-    // the next tile (a repeat of the last one past the end, never used)
-    load_tile(std::integral_constant<int, 1 - bf>{}, min(it + 1, ntiles - 1));
+    // tile it + NBUF - 1 into the buffer freed by tile it - 1 (past the end: a
+    // repeat of the last tile, never used)
+    load_tile(std::integral_constant<int, (bf + NBUF - 1) % NBUF>{}, min(it + NBUF - 1, ntiles - 1));
 
     float sc[2][4];
 #pragma unroll
@@ -212,20 +248,35 @@ void headwise_stream_kernel(HeadwiseParams p) {
       for (int e = 0; e < 4; ++e) {
         float s = 0.f;
         if constexpr (ROPE) {
+          // rotation by the in-tile offset o = 16 hf + 4 lg + e
+          f32x4 rc, rs;
+          if constexpr (RT_LDS) {
+            rc = rt[0][16 * hf + 4 * lg + e][li];
+            rs = rt[1][16 * hf + 4 * lg + e][li];
+          } else {
+            rc = oc[hf][e];
+            rs = os[hf][e];
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float c = rc[hf][e][j], sn = rs[hf][e][j];
-            const float k0 = kacc[j][e], k1 = kacc[j + 4][e];
-            s = fmaf(k0 * c - k1 * sn, qr[j], s);
-            s = fmaf(k1 * c + k0 * sn, qr[j + 4], s);
+            const float c = rc[j], sn = rs[j];
+            const float z0 = fmaf(y0[j], c, y1[j] * sn), z1 = fmaf(y1[j], c, -(y0[j] * sn));
+            s = fmaf(kacc[j][e], z0, s);
+            s = fmaf(kacc[j + 4][e], z1, s);
           }
         } else {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) s = fmaf(kacc[nb][e], qr[nb], s);
         }
-        s = sum16(s);
-        sc[hf][e] = t0 + 16 * hf + 4 * lg + e < L ? s : -INFINITY;
+        sc[hf][e] = sum16(s);
       }
+    }
+    if (t0 + kHT > L) {   // the partial last tile: tokens past L drop out
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (t0 + 16 * hf + 4 * lg + e >= L) sc[hf][e] = -INFINITY;
     }
 
     // ---- online softmax over the 32 tokens (each score sits in 16 lanes)
@@ -264,22 +315,29 @@ void headwise_stream_kernel(HeadwiseParams p) {
     __builtin_amdgcn_wave_barrier();
 
     // ---- O~ = alpha O~ + p^T C_V over this lane's two tokens
+    if (alpha < 1.f) {   // the running max moved (uniform over the wavefront)
+#pragma unroll
+      for (int v = 0; v < KBV; ++v)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ov[v][c] *= alpha;
+    }
 #pragma unroll
     for (int v = 0; v < KBV; ++v) {
       const u32x4 w0 = tl[bf][0][KBK + v], w1 = tl[bf][1][KBK + v];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        float lo = fmaf(p0, __uint_as_float(w0[c] << 16), ov[v][2 * c] * alpha);
-        float hi = fmaf(p0, __uint_as_float(w0[c] & 0xFFFF0000u), ov[v][2 * c + 1] * alpha);
-        ov[v][2 * c] = fmaf(p1, __uint_as_float(w1[c] << 16), lo);
-        ov[v][2 * c + 1] = fmaf(p1, __uint_as_float(w1[c] & 0xFFFF0000u), hi);
+        ov[v][2 * c] = fmaf(p1, __uint_as_float(w1[c] << 16), fmaf(p0, __uint_as_float(w0[c] << 16), ov[v][2 * c]));
+        ov[v][2 * c + 1] = fmaf(p1, __uint_as_float(w1[c] & 0xFFFF0000u),
+                                fmaf(p0, __uint_as_float(w0[c] & 0xFFFF0000u), ov[v][2 * c + 1]));
       }
     }
   };
 
-  for (int it = 0; it < ntiles; it += 2) {
+  for (int it = 0; it < ntiles; it += NBUF) {
     body(std::integral_constant<int, 0>{}, it);
     if (it + 1 < ntiles) body(std::integral_constant<int, 1>{}, it + 1);
+    if constexpr (NBUF == 3)
+      if (it + 2 < ntiles) body(std::integral_constant<int, 2 % NBUF>{}, it + 2);
   }
 
   // ---- the split's partial state: O~ summed over the 16 lanes (tokens) of each group
@@ -300,34 +358,50 @@ void headwise_stream_kernel(HeadwiseParams p) {
 }
 
 // One wavefront per (sequence, head): O~ = sum_s 2^(m_s - M) O~_s / sum_s 2^(m_s - M) l_s,
-// then O = O~ B_Vh.
-template <typename OT>
+// then O = O~ B_Vh.  Splits are spread over the lanes for the max and the
+// denominator; lane c then sums column c of O~ over the splits.
+template <typename OT, int RV>
 __global__ __launch_bounds__(256) void headwise_merge_kernel(const float *__restrict__ part,
                                                              const uint16_t *__restrict__ BV,
-                                                             OT *__restrict__ O, int b, int heads,
-                                                             int S, int rv) {
-  __shared__ float om[4][kHd];
+                                                             OT *__restrict__ O, int b, int heads, int S) {
+  constexpr int PW = RV + 4;
+  __shared__ float om[4][RV];
   const int wl = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + wl;
-  if (w >= b * heads) return;   // uniform per wavefront; barriers below are wave-local
+  if (w >= b * heads) return;   // uniform per wavefront; the LDS use below is wave-local
   const int seq = w / heads, h = w % heads;
+  const float *base = part + (static_cast<int64_t>(seq) * S * heads + h) * PW;
+  const int64_t sstride = static_cast<int64_t>(heads) * PW;
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part[((static_cast<int64_t>(seq) * S + s) * heads + h) * (rv + 4)]);
-  float den = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float *src = part + ((static_cast<int64_t>(seq) * S + s) * heads + h) * (rv + 4);
-    const float wgt = src[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(src[0] - M);
-    den = fmaf(wgt, src[1], den);
-    if (lane < rv) o0 = fmaf(wgt, src[4 + lane], o0);
-    if (lane + 64 < rv) o1 = fmaf(wgt, src[4 + 64 + lane], o1);
+  for (int s = lane; s < S; s += kWave) M = fmaxf(M, base[s * sstride]);
+  M = group_max<kWave>(M);
+  float den = 0.f;
+  for (int s = lane; s < S; s += kWave) {
+    const float ms = base[s * sstride];
+    den += ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M) * base[s * sstride + 1];
   }
+  den = group_sum<kWave>(den);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  om[wl][lane] = o0 * inv;
-  om[wl][lane + 64] = o1 * inv;
+  constexpr int CPL = (RV + kWave - 1) / kWave;   // O~ columns per lane
+  float acc[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float *src = base + s * sstride;
+    const float ms = src[0];
+    const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+      if (lane + kWave * k < RV) acc[k] = fmaf(wgt, src[4 + lane + kWave * k], acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < CPL; ++k)
+    if (lane + kWave * k < RV) om[wl][lane + kWave * k] = acc[k] * inv;
   __builtin_amdgcn_wave_barrier();
-  const uint16_t *bv = BV + static_cast<int64_t>(h) * rv * kHd;
+  const uint16_t *bv = BV + static_cast<int64_t>(h) * RV * kHd;
   float a0 = 0.f, a1 = 0.f;
-  for (int c = 0; c < rv; ++c) {
+#pragma unroll 16
+  for (int c = 0; c < RV; ++c) {
     const float oc = om[wl][c];
     a0 = fmaf(oc, bf16_to_f32(bv[c * kHd + lane]), a0);
     a1 = fmaf(oc, bf16_to_f32(bv[c * kHd + 64 + lane]), a1);
@@ -340,6 +414,21 @@ __global__ __launch_bounds__(256) void headwise_merge_kernel(const float *__rest
     out[lane] = a0;
     out[64 + lane] = a1;
   }
+}
+
+template <typename OT>
+hipError_t launch_hw_merge(const float *part, const void *BV, void *O, int b, int heads, int S, int rv,
+                           hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((b * heads + 3) / 4)), block(256);
+  const uint16_t *bv = static_cast<const uint16_t *>(BV);
+  OT *o = static_cast<OT *>(O);
+  switch (rv) {
+    case 32: headwise_merge_kernel<OT, 32><<<grid, block, 0, s>>>(part, bv, o, b, heads, S); break;
+    case 64: headwise_merge_kernel<OT, 64><<<grid, block, 0, s>>>(part, bv, o, b, heads, S); break;
+    case 96: headwise_merge_kernel<OT, 96><<<grid, block, 0, s>>>(part, bv, o, b, heads, S); break;
+    default: headwise_merge_kernel<OT, 128><<<grid, block, 0, s>>>(part, bv, o, b, heads, S); break;
+  }
+  return hipGetLastError();
 }
 
 template <int KBK, int KBV>
@@ -404,14 +493,8 @@ hipError_t launch_decode_headwise(const HeadwiseArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   LaunchTimer t("headwise_merge", s);
-  const dim3 mgrid(static_cast<unsigned>((a.b * a.heads + 3) / 4)), block(256);
-  if (a.o_dtype == QSVD_BF16)
-    headwise_merge_kernel<uint16_t><<<mgrid, block, 0, s>>>(hp.part, static_cast<const uint16_t *>(a.BV),
-                                                            static_cast<uint16_t *>(a.O), a.b, a.heads, S, a.rv);
-  else
-    headwise_merge_kernel<float><<<mgrid, block, 0, s>>>(hp.part, static_cast<const uint16_t *>(a.BV),
-                                                         static_cast<float *>(a.O), a.b, a.heads, S, a.rv);
-  return hipGetLastError();
+  if (a.o_dtype == QSVD_BF16) return launch_hw_merge<uint16_t>(hp.part, a.BV, a.O, a.b, a.heads, S, a.rv, s);
+  return launch_hw_merge<float>(hp.part, a.BV, a.O, a.b, a.heads, S, a.rv, s);
 }
 
 }  // namespace qsvd
