@@ -9,6 +9,11 @@ split-L stream, merge, finalize).  value = decode tokens/s = b / step time.
 Explicit leg: the same step with K and V rebuilt explicitly on chip and
 rotary positions (qsvd_decode_attn_explicit), against the bf16 MFMA peak.
 
+Per-head latent leg: the same attention shape with per-head latents (each
+head caches rk = 64 key and rv = 64 value latents per token; keys rebuilt on
+chip with RoPE, B_Vh applied after the softmax; qsvd_decode_attn_headwise),
+against the HBM peak.
+
 Prefill leg: the shared down-projection at W8A8, X [16384][4096] int8 (H1
 rotated, per-token scales) times W^d [4096][1536] int8 (per-column scales),
 reported as TOPS; plus the rotate+quantise steps around it.
@@ -52,6 +57,8 @@ def parse():
     ap.add_argument("--chain", action="store_true", help="also time the 24-layer prefill chain")
     ap.add_argument("--no-explicit", action="store_true",
                     help="skip the explicit K/V reconstruction (RoPE) decode leg")
+    ap.add_argument("--no-headwise", action="store_true",
+                    help="skip the per-head latent (RoPE) decode leg")
     return ap.parse_args()
 
 
@@ -174,6 +181,11 @@ def main():
         log(f"[bench] explicit K/V + RoPE decode: {ms_e * 1e3:.1f} us/step, {tf:.0f} TFLOP/s")
         del ws_e, Wk_t, Wv_t
 
+    # ------------------------------------------------------------------ per-head latent leg
+    headwise = None
+    if not args.no_headwise:
+        headwise = headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args)
+
     # ------------------------------------------------------------------ prefill
     prefill = None
     if not args.no_prefill:
@@ -253,6 +265,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "explicit": explicit,
+        "headwise": headwise,
     }
     print(json.dumps(out), flush=True)
 
@@ -284,6 +297,54 @@ def chain_leg(q, torch, np, synth, xq, xs, M, E, steps):
     ms = timed(run, steps, 1)
     ops = sum(2.0 * M * E * rl + 2.0 * M * rl * 2 * E for rl in ranks)
     return {"layers": len(ranks), "ms": round(ms, 3), "tops": round(ops / (ms * 1e-3) / 1e12, 1)}
+
+
+def headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args, rk=64, rv=64):
+    """Per-head latents at the decode leg's shape: C [b][L][heads][rk + rv] bf16, RoPE
+    tables for L positions; the step is qsvd_decode_attn_headwise (stream + merge)."""
+    t0 = time.time()
+    hc = synth.headwise_case(b, L, heads, d, rk, rv, seed=7)
+    log(f"[bench] generated per-head latent inputs in {time.time() - t0:.1f}s")
+    C0 = bf(hc.C)
+    hc.C = None
+    copies = [C0] + [C0.clone() for _ in range(max(args.copies, 1) - 1)]
+    qv, BK, BV = bf(hc.q), bf(hc.BK_t), bf(hc.BV)
+    rc, rs = (dev(t) for t in synth.rope_tables(L, d))
+    O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(q.qsvd_decode_headwise_workspace_bytes(b, L, heads, d, rk, rv, 0),
+                     dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, tables in (("rope", (rc, rs)), ("plain", (None, None))):
+        def step(i):
+            q.qsvd_decode_attn_headwise(qv, q.BF16, copies[i % len(copies)], q.BF16, BK, BV, q.BF16,
+                                        b, L, heads, d, rk, rv, hc.softmax_scale, tables[0],
+                                        tables[1], 0, O, q.BF16, ws)
+        n = max(args.steps // 2, 5)
+        ms = timed(step, n, 2)
+        with q.timing(max_launches=4 * n + 8) as tm:
+            for i in range(n):
+                step(i)
+        torch.cuda.synchronize()
+        res[name] = (ms, {k: v[1] / v[0] for k, v in tm.result.items()})
+    cache_bytes = b * L * heads * (rk + rv) * 2
+    ms, kern = res["rope"]
+    stream_ms = kern.get("headwise_stream", float("nan"))
+    achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
+    step_bytes = cache_bytes + heads * d * (rk + rv) * 2 + 2 * b * heads * d * 2
+    log(f"[bench] per-head latent decode (RoPE): {ms * 1e3:.1f} us/step; kernels (us): " +
+        ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kern.items()) +
+        f"; without RoPE {res['plain'][0] * 1e3:.1f} us/step")
+    del copies, C0
+    return {"workload": f"per-head latents (WSVD form), 32 heads x 128, rk = rv = {rk}, b = {b}, "
+                        f"L = {L}, bf16 cache, RoPE (qsvd_decode_attn_headwise)",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(b / (ms * 1e-3), 1),
+            "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+            "no_rope_ms_per_step": round(res["plain"][0], 4),
+            "roofline": {"bound": "hbm", "kernel": "headwise_stream", "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": cache_bytes}}
 
 
 def dev_t(torch, np, a):

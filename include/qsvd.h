@@ -242,7 +242,11 @@ qsvd_status_t qsvd_decode_attn_explicit(const void *q, qsvd_dtype_t q_dtype, con
  *   rope_cos, rope_sin
  *              NULL (no rotation) or float32 tables [P][d/2], P >= L, with the
  *              same meaning and rotation as in qsvd_decode_attn_explicit
- *              (cached token t at position t, the query at L - 1).
+ *              (cached token t at position t, the query at L - 1).  Rotations
+ *              are composed: a 32-token tile starting at t0 reads row t0 and
+ *              the rows 0 .. 31, so row t must be the rotation by t * theta_i
+ *              (angles linear in the position, as in RoPE with any base or a
+ *              linearly scaled theta).
  *   splits     L-splits per sequence (0: a default that fills the device;
  *              at most 1024, clipped to the number of 32-token tiles).
  *   O          [b][heads][d], o_dtype BF16 or F32.
