@@ -62,11 +62,15 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def source_hash(name: str) -> str:
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "rank_latent_attention_amd", "csrc", "decode.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "rank_latent_attention_amd", "csrc", name), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    return source_hash("decode.hip")
 
 
 def timed(fn, steps, warmup):
@@ -331,6 +335,13 @@ def headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args, rk=64, rv=64):
     stream_ms = kern.get("headwise_stream", float("nan"))
     achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
     step_bytes = cache_bytes + heads * d * (rk + rv) * 2 + 2 * b * heads * d * 2
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        if c.get("headwise_hip_sha256_16") == source_hash("headwise.hip"):
+            k = c.get("other_kernels", {}).get(f"headwise_stream_kernel<{rk // 32}, {rv // 32}, true>")
+            if k:
+                traffic = k["hbm_read_bytes"] + k["hbm_write_bytes"]
     log(f"[bench] per-head latent decode (RoPE): {ms * 1e3:.1f} us/step; kernels (us): " +
         ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kern.items()) +
         f"; without RoPE {res['plain'][0] * 1e3:.1f} us/step")
@@ -343,7 +354,7 @@ def headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args, rk=64, rv=64):
             "no_rope_ms_per_step": round(res["plain"][0], 4),
             "roofline": {"bound": "hbm", "kernel": "headwise_stream", "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                          "algorithmic_bytes": cache_bytes}}
 
 
