@@ -77,15 +77,15 @@ struct HeadwiseParams {
 // Launch shape of one (rk, rv, RoPE) instance.  Registers a wavefront needs
 // (B_Kh fragments, two tile buffers, K accumulators, O~ shares, the rotated
 // query, addresses) decide between two wavefronts per SIMD (<= 256) and one
-// (<= 512).  The in-tile RoPE rows (64 values a lane) sit in LDS when that
-// buys the second wavefront, else in registers; a lone wavefront keeps two
-// tiles in flight (three buffers) when its registers allow.
+// (<= 512).  The in-tile RoPE rows (32 packed cos / sin pairs a lane) sit in
+// LDS when that buys the second wavefront, else in registers; a lone
+// wavefront keeps two tiles in flight (three buffers) when its registers allow.
 template <int KBK, int KBV, bool ROPE>
 struct HwShape {
   static constexpr int kBase = 32 * KBK + 16 * (KBK + KBV) + 8 * KBV + 104;
-  static constexpr bool kRowsInLds = ROPE && kBase + 8 <= 256;
-  static constexpr int kOcc = kBase + (ROPE ? (kRowsInLds ? 8 : 64) : 0) <= 256 ? 2 : 1;
-  static constexpr int kBufs = kOcc == 1 && kBase + (ROPE ? 64 : 0) + 8 * (KBK + KBV) <= 440 ? 3 : 2;
+  static constexpr bool kRowsInLds = ROPE && kBase + 32 > 256 && kBase + 8 <= 256;
+  static constexpr int kOcc = kBase + (ROPE ? (kRowsInLds ? 8 : 32) : 0) <= 256 ? 2 : 1;
+  static constexpr int kBufs = kOcc == 1 && kBase + (ROPE ? 32 : 0) + 8 * (KBK + KBV) <= 440 ? 3 : 2;
 };
 
 // Head dimension held by lane li in column block nb of K: lane li owns
@@ -93,6 +93,18 @@ struct HwShape {
 // (blocks 4-7), so a RoPE pair (i, i + 64) sits in one lane and the lane's
 // cos / sin values of a position are one 16-byte load.
 __device__ __forceinline__ int hw_dim(int nb, int li) { return (nb >> 2) * 64 + 4 * li + (nb & 3); }
+
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four (cos, sin) pairs of one table row as f16 pairs (round to nearest even).
+__device__ __forceinline__ u32x4 rope_pairs(const float *c, const float *s) {
+  const f32x4 cv = *reinterpret_cast<const f32x4 *>(c), sv = *reinterpret_cast<const f32x4 *>(s);
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{cv[j], sv[j]}, h16x2));
+  return out;
+}
 
 template <int KBK, int KBV, bool ROPE>
 __global__ __launch_bounds__(256)
@@ -103,8 +115,8 @@ void headwise_stream_kernel(HeadwiseParams p) {
   constexpr int NBUF = HwShape<KBK, KBV, ROPE>::kBufs;
   constexpr bool RT_LDS = HwShape<KBK, KBV, ROPE>::kRowsInLds;
   __shared__ float pbuf[kHeadsPerWg][kHT];
-  // RoPE rows 0 .. 31 (cos, sin), the in-tile rotations, shared by the heads
-  __shared__ f32x4 rt[RT_LDS ? 2 : 1][RT_LDS ? kHT : 1][16];
+  // RoPE rows 0 .. 31, the in-tile rotations, as f16 (cos, sin) pairs; shared by the heads
+  __shared__ u32x4 rt[RT_LDS ? kHT : 1][16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -121,10 +133,10 @@ void headwise_stream_kernel(HeadwiseParams p) {
   const int64_t seq = task / (G * p.S);
   const int h = grp * kHeadsPerWg + wave;
   if constexpr (RT_LDS) {
-    for (int i = threadIdx.x; i < 2 * kHT * 16; i += blockDim.x) {
-      const int tb = i / (kHT * 16), row = (i / 16) % kHT, c4 = i % 16;
+    for (int i = threadIdx.x; i < kHT * 16; i += blockDim.x) {
+      const int row = i / 16, c4 = i % 16;
       const int64_t r = row < p.L ? row : p.L - 1;   // rows past L: never used unmasked
-      rt[tb][row][c4] = *reinterpret_cast<const f32x4 *>((tb ? p.rope_sin : p.rope_cos) + r * (kHd / 2) + 4 * c4);
+      rt[row][c4] = rope_pairs(p.rope_cos + r * (kHd / 2) + 4 * c4, p.rope_sin + r * (kHd / 2) + 4 * c4);
     }
     __syncthreads();   // the only barrier: before any wavefront leaves
   }
@@ -189,7 +201,7 @@ void headwise_stream_kernel(HeadwiseParams p) {
     }
   }
   // in-tile RoPE rows in registers: offset o = 16 hf + 4 lg + e of this lane's tokens
-  f32x4 oc[2][4], os[2][4];
+  u32x4 ocs[2][4];
   if constexpr (ROPE && !RT_LDS) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
@@ -197,8 +209,7 @@ void headwise_stream_kernel(HeadwiseParams p) {
       for (int e = 0; e < 4; ++e) {
         const int64_t o = 16 * hf + 4 * lg + e;
         const int64_t off = (o < L ? o : L - 1) * (kHd / 2) + 4 * li;
-        oc[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_cos + off);
-        os[hf][e] = *reinterpret_cast<const f32x4 *>(p.rope_sin + off);
+        ocs[hf][e] = rope_pairs(p.rope_cos + off, p.rope_sin + off);
       }
   }
 
@@ -215,15 +226,19 @@ void headwise_stream_kernel(HeadwiseParams p) {
     // RoPE: rot(K_t, t) . rot(q, L - 1) = K_t . R(-o) y with y = R(-t0) rot(q, L - 1)
     // for token t = t0 + o; rotations by position compose (angles are t theta_i),
     // so a tile reads table row t0 besides the in-tile rows 0 .. 31 held all along
-    float y0[4], y1[4];
+    // (y0, y1) and (y1, -y0) as f16 pairs: R(-o) y is then two dot2 products
+    // with the f16 (cos, sin) pair of the offset
+    h16x2 ya[4], yb[4];
     if constexpr (ROPE) {
       const int64_t off = t0 * (kHd / 2) + 4 * li;
       const f32x4 c0 = *reinterpret_cast<const f32x4 *>(p.rope_cos + off);
       const f32x4 s0 = *reinterpret_cast<const f32x4 *>(p.rope_sin + off);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        y0[j] = fmaf(qr[j], c0[j], qr[j + 4] * s0[j]);
-        y1[j] = fmaf(qr[j + 4], c0[j], -(qr[j] * s0[j]));
+        const float y0 = fmaf(qr[j], c0[j], qr[j + 4] * s0[j]);
+        const float y1 = fmaf(qr[j + 4], c0[j], -(qr[j] * s0[j]));
+        ya[j] = __builtin_convertvector(f32x2{y0, y1}, h16x2);
+        yb[j] = __builtin_convertvector(f32x2{y1, -y0}, h16x2);
       }
     }
     // tile it + NBUF - 1 into the buffer freed by tile it - 1 (past the end: a
@@ -249,18 +264,17 @@ void headwise_stream_kernel(HeadwiseParams p) {
         float s = 0.f;
         if constexpr (ROPE) {
           // rotation by the in-tile offset o = 16 hf + 4 lg + e
-          f32x4 rc, rs;
-          if constexpr (RT_LDS) {
-            rc = rt[0][16 * hf + 4 * lg + e][li];
-            rs = rt[1][16 * hf + 4 * lg + e][li];
-          } else {
-            rc = oc[hf][e];
-            rs = os[hf][e];
-          }
+          u32x4 cs;
+          if constexpr (RT_LDS)
+            cs = rt[16 * hf + 4 * lg + e][li];
+          else
+            cs = ocs[hf][e];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float c = rc[j], sn = rs[j];
-            const float z0 = fmaf(y0[j], c, y1[j] * sn), z1 = fmaf(y1[j], c, -(y0[j] * sn));
+            const uint32_t csw = cs[j];   // a named scalar: bit_cast of a vector element reads element 0
+            const h16x2 csj = __builtin_bit_cast(h16x2, csw);
+            const float z0 = __builtin_amdgcn_fdot2(ya[j], csj, 0.f, false);   // y0 c + y1 s
+            const float z1 = __builtin_amdgcn_fdot2(yb[j], csj, 0.f, false);   // y1 c - y0 s
             s = fmaf(kacc[j][e], z0, s);
             s = fmaf(kacc[j + 4][e], z1, s);
           }
