@@ -13,19 +13,21 @@
 // BV[heads][rv][128].
 //
 // headwise_stream_kernel: workgroup (sequence, split, 4 heads), one wavefront
-// per head and nothing shared between wavefronts.  A wavefront keeps its head's
-// B_Kh fragments in registers for the whole split and, per 32-token tile:
+// per head; past the staging of the RoPE rows the wavefronts share nothing.  A
+// wavefront keeps its head's B_Kh fragments in registers for the whole split
+// and, per 32-token tile:
 //   1. 16-byte buffer loads of the tile's key and value latents of its head,
-//      one tile ahead (rows past L read as zero and are masked);
+//      one or two tiles ahead (rows past L read as zero and are masked);
 //   2. K (32 x 128) = C_K (32 x rk) B_Kh with v_mfma_f32_16x16x32_bf16, the
 //      latent rows straight from the load registers as the A operand;
 //   3. RoPE: dimension i pairs with i + 64, both in the same lane (column
-//      blocks nb and nb + 4), rotated with the caller's cos / sin tables;
-//   4. scores (dot with the rotated, pre-scaled query: 16-lane DPP sums),
-//      the online softmax of the split (log2 units);
-//   5. O~ += p^T C_V: each lane accumulates its own tokens' value columns;
-//      p moves from the score lanes to the value lanes through 128 bytes of
-//      the wavefront's LDS.
+//      blocks nb and nb + 4).  Rotations compose, so the query is turned back
+//      to the tile start once per tile (table row t0) and then by each token's
+//      offset inside the tile (rows 0 .. 31, read once), with f16 dot2 products;
+//   4. scores (16-lane DPP sums), the online softmax of the split (log2 units);
+//   5. O~ += p^T C_V: each lane accumulates its own tokens' value columns
+//      (rescaled only when the running max moves); p moves from the score
+//      lanes to the value lanes through 128 bytes of the wavefront's LDS.
 // The lanes' O~ shares are summed once per split; (m, l, O~) go to the
 // workspace.  headwise_merge_kernel combines the splits by their log-sum-exp
 // weights and applies B_Vh.
