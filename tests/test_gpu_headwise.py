@@ -105,3 +105,40 @@ def test_headwise_full_size_sampled():
         err = oracle.rel_l2(got[s], ref)
         say(f"  sequence {s}: rel-L2 {err:.2e}")
         assert err <= TOL
+
+
+EDGE_SHAPES = [
+    # b, L, heads, rk, rv
+    (1, 32, 1, 32, 32),       # one full tile, one head
+    (2, 64, 3, 64, 96),       # two full tiles, no partial tile
+    (1, 33, 4, 128, 32),      # one token past a tile
+    (5, 700, 12, 32, 64),     # several head groups and sequences
+]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "b{}L{}h{}rk{}rv{}".format(*s))
+def test_headwise_edges(shape):
+    b, L, heads, rk, rv = shape
+    say(f"case: headwise edge b={b} L={L} heads={heads} rk={rk} rv={rv}")
+    cs = synth.headwise_case(b, L, heads, 128, rk, rv, seed=3 * L + heads)
+    for rope in (False, True):
+        got = run_headwise(cs, rope)
+        err = oracle.rel_l2(got, oracle_out(cs, rope))
+        say(f"  rope={rope}: rel-L2 {err:.2e}")
+        assert err <= TOL
+
+
+def test_headwise_longer_rope_tables():
+    """Tables with more rows than cached tokens (a runtime's preallocated
+    maximum length): only rows 0 .. L-1 matter, the result is unchanged."""
+    import torch
+    cs = synth.headwise_case(2, 150, 4, 128, 64, 64, seed=12)
+    want = run_headwise(cs, rope=True, o_dtype=q.F32)
+    c, s = synth.rope_tables(cs.L + 333, cs.d)
+    O = empty((cs.b, cs.heads, cs.d), torch.float32)
+    ws = workspace(q.qsvd_decode_headwise_workspace_bytes(cs.b, cs.L, cs.heads, cs.d, cs.rk, cs.rv, 0))
+    q.qsvd_decode_attn_headwise(dev(cs.q), q.BF16, dev(cs.C), q.BF16, dev(cs.BK_t), dev(cs.BV), q.BF16,
+                                cs.b, cs.L, cs.heads, cs.d, cs.rk, cs.rv, cs.softmax_scale, dev(c), dev(s),
+                                0, O, q.F32, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(O), want)
