@@ -346,7 +346,11 @@ __device__ __forceinline__ float dpp_reduce(float v) {
   v = dpp_step<0xB1, MAX>(v);   // quad_perm [1,0,3,2]
   v = dpp_step<0x4E, MAX>(v);   // quad_perm [2,3,0,1]
   v = dpp_step<0x141, MAX>(v);  // row_half_mirror
-  if constexpr (N == 16) v = dpp_step<0x140, MAX>(v);  // row_mirror
+  if constexpr (N >= 16) v = dpp_step<0x140, MAX>(v);  // row_mirror
+  if constexpr (N == 32) {      // the neighbouring 16-lane row
+    const float y = __shfl_xor(v, 16, 64);
+    v = MAX ? fmaxf(v, y) : v + y;
+  }
   return v;
 }
 
@@ -358,7 +362,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 
 // Template parameters: cache format CT, NHB 16-head blocks per workgroup, NKB
 // 32-column K blocks per wavefront (RW = 32 NKB columns), T tokens per tile
-// (32 or 16), D tiles of loads in flight (1 or 2; register staging).  The
+// (16, 32, or 64 for quantised caches, whose codes stage in few registers),
+// D tiles of loads in flight (1 or 2; register staging).  The
 // wavefront count W = blockDim.x / 64 <= 8 satisfies r = W * RW.
 template <int CT, int NHB, int NKB, int T, int D>
 __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
@@ -370,12 +375,13 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   constexpr int NJB = NKB * 2;          // 16-column blocks of O~
   constexpr int RW = NKB * 32;          // columns per wavefront
   constexpr int RS = ct_row_stride(NKB);
-  constexpr int PPL = T / 4;            // tokens per lane in the value product operands
+  constexpr int PPL = T == 16 ? 4 : 8;  // tokens per lane in a value product operand
+  constexpr int NKS = T == 16 ? 1 : T / 32;   // 32-token K steps of the value product
   constexpr int SPR = sp_row(T);
   constexpr int HGP = NHB * 16;
   constexpr int MAXW = 8;
   static_assert(NKB % KPL == 0, "wavefront columns must be whole 16-byte loads");
-  static_assert(T == 16 || T == 32, "tile");
+  static_assert(T == 16 || T == 32 || T == 64, "tile");
   static_assert(D == 1 || D == 2, "prefetch depth");
   static_assert(HGP * RW * 2 <= T * RS, "the output rows are staged in the wavefront's C tile");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   uint8_t *ct = smem + static_cast<size_t>(wave) * T * RS;
   float *spart = reinterpret_cast<float *>(smem + static_cast<size_t>(W) * T * RS);
   uint16_t *pl = reinterpret_cast<uint16_t *>(spart + static_cast<size_t>(W) * HGP * SPR);
-  float *alpha_s = reinterpret_cast<float *>(pl + NHB * 64 * PPL);
+  float *alpha_s = reinterpret_cast<float *>(pl + NHB * 64 * (T / 4));
   float *m_s = alpha_s + HGP;
   float *l_s = m_s + HGP;
 
@@ -581,8 +587,10 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         l_s[h] = fmaf(l_s[h], alpha, psum);
         alpha_s[h] = alpha;
       }
-      // P as the B operand of the value product: lane 16 (t / PPL) + h % 16, element t % PPL
-      uint16_t *pdst = pl + ((h >> 4) * 64 + 16 * (t0 / PPL) + (h & 15)) * PPL + (t0 % PPL);
+      // P as the B operand of the value product: K step t / 32 (T >= 32), lane
+      // 16 ((t % 32) / PPL) + h % 16, element t % PPL
+      const int ks = T == 16 ? 0 : t0 >> 5, tk = T == 16 ? t0 : t0 & 31;
+      uint16_t *pdst = pl + ((ks * NHB + (h >> 4)) * 64 + 16 * (tk / PPL) + (h & 15)) * PPL + (tk % PPL);
       *reinterpret_cast<uint32_t *>(pdst) = pp;
     }
     __syncthreads();
@@ -602,12 +610,16 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
     // A operand: column 16 jb + lane % 16, tokens PPL g + (0..PPL-1), by
     // transposing 8-byte reads of 4 tokens each (lane i of a 16-lane group
     // supplies row i / 4 and columns 4 (i % 4) .. +3 of a 4 x 16 block).
-    const uint8_t *trb = ct + (PPL * lg + (li >> 2)) * RS + (4 * (li & 3)) * 2;
-    if constexpr (T == 32) {
+    if constexpr (T >= 32) {
+#pragma unroll
+     for (int ks = 0; ks < NKS; ++ks) {
+      // K step ks: tokens 32 ks + PPL g + (0..PPL-1)
+      const uint8_t *trb = ct + (32 * ks + PPL * lg + (li >> 2)) * RS + (4 * (li & 3)) * 2;
       bf16x8 pb[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        pb[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(pl + (hb * 64 + lane) * PPL));
+        pb[hb] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4 *>(pl + ((ks * NHB + hb) * 64 + lane) * PPL));
       // column blocks in groups of VB: all transposing reads of a group are
       // issued before its products
       constexpr int VB = (NJB % 4 == 0) ? 4 : ((NJB % 3 == 0) ? 3 : 2);
@@ -628,7 +640,9 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
             oacc[hb][jg + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hb], oacc[hb][jg + k], 0, 0, 0);
         }
       }
+     }
     } else {
+      const uint8_t *trb = ct + (PPL * lg + (li >> 2)) * RS + (4 * (li & 3)) * 2;
       bf16x4 pb[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
@@ -1047,8 +1061,11 @@ hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
 
 template <int CT, int NHB, int NKB>
 hipError_t launch_stream_tile(const StreamParams &sp, const MfmaShape &sh, hipStream_t s) {
+  if constexpr (CT != CT_BF16 && NKB <= 8) {
+    if (sh.T == 64) return launch_stream_t<CT, NHB, NKB, 64, 1>(sp, sh.W, s);
+  }
   if constexpr (NHB == 2) {
-    return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);  // mfma_shape pairs NHB = 2 with T = 32
+    return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);  // mfma_shape pairs NHB = 2 with T >= 32
   } else {
     if (sh.T == 32) return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);
     return launch_stream_t<CT, NHB, NKB, 16, 2>(sp, sh.W, s);
@@ -1210,6 +1227,10 @@ bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
     s.NKB = nkb;
     s.NHB = (heads > 16 && nkb <= 6 && stream_lds_bytes(W, 2, nkb, 32) <= kMaxLds) ? 2 : 1;
     s.T = (nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32) <= kMaxLds) ? 32 : 16;
+    // quantised codes stage in few registers: a 64-token tile halves the
+    // per-token share of the barriers and the softmax where LDS holds it
+    if (c_dtype != QSVD_BF16 && s.T == 32 && nkb <= 8 && stream_lds_bytes(W, s.NHB, nkb, 64) <= kMaxLds)
+      s.T = 64;
     // tuning override of the tile (32: one tile of loads in flight, 16: two)
     static const int tile_env = [] {
       const char *e = std::getenv("QSVD_STREAM_TILE");
