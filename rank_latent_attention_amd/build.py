@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsvd.so")
 
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "decode.hip", "explicit.hip", "headwise.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "decode.hip", "decode_wide.hip", "explicit.hip", "headwise.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -1183,7 +1183,7 @@ hipError_t launch_merge_mfma(const DecodeArgs &a, const DecodePlan &p, const uin
   if (e != hipSuccess) return e;
   kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
       opart, ml, static_cast<const WT *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
-      p.splits, a.r / p.shape.W);
+      p.splits, p.rw);
   return hipGetLastError();
 }
 
@@ -1267,6 +1267,15 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
     S = std::min<int64_t>(std::min<int64_t>(S, tiles_all), kMaxSplits);
     p.chunk = 0;
     p.splits = static_cast<int>(S);
+    p.rw = r / sh.W;
+    // many heads over a wide latent: two passes that each read the cache once
+    // beat a single pass whose head groups read it three or more times
+    if (wide_applies(r, heads, c_dtype, G)) {
+      p.wide = true;
+      wide_plan(b, L, r, heads, &p.wp);
+      p.splits = p.wp.splits;
+      p.rw = p.wp.rw;
+    }
   } else {
     p.head_groups = heads;
     p.group_heads = 1;
@@ -1290,6 +1299,7 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
   const int JC = (r + kMergeRows - 1) / kMergeRows;
   const size_t opj = align256(static_cast<size_t>(JC) * b * heads * d * sizeof(float));
   p.part_bytes = opart + ml + opj;
+  if (p.wide) p.part_bytes += align256(p.wp.s_bytes) + align256(p.wp.m1_bytes);
   p.total = p.qt_bytes + p.part_bytes;
   return p;
 }
@@ -1323,8 +1333,31 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
     if (e != hipSuccess) return e;
   }
 
-  // ---- stream
-  {
+  // ---- stream (two passes for wide latents with many heads)
+  if (p.wide) {
+    uint8_t *wbase = reinterpret_cast<uint8_t *>(opj) +
+                     align256(static_cast<size_t>((a.r + kMergeRows - 1) / kMergeRows) * a.b * a.heads * a.d * sizeof(float));
+    WideArgs wa{};
+    wa.C = a.C;
+    wa.qt = static_cast<const uint16_t *>(qt);
+    wa.S = reinterpret_cast<float *>(wbase);
+    wa.m1 = reinterpret_cast<float *>(wbase + align256(p.wp.s_bytes));
+    wa.opart = static_cast<uint16_t *>(opart);
+    wa.ml = ml;
+    wa.L = a.L;
+    wa.Lp = p.wp.Lp;
+    wa.chunk1 = p.wp.chunk1;
+    wa.chunk3 = p.wp.chunk3;
+    wa.b = a.b;
+    wa.r = a.r;
+    wa.heads = a.heads;
+    wa.nchunk1 = p.wp.nchunk1;
+    wa.splits = p.splits;
+    e = launch_wide_scores(wa, s);
+    if (e != hipSuccess) return e;
+    e = launch_wide_values(wa, s);
+    if (e != hipSuccess) return e;
+  } else {
     LaunchTimer t("decode_stream", s);
     if (!p.mfma) {
       const int maxj = (a.r + 63) / 64;

@@ -1,0 +1,426 @@
+// Two-pass decode for wide latents with many heads (bf16 caches, gfx950).
+//
+// QSVD paper notes, "Key design": K = C W^u_k and V = C W^u_v are rebuilt from
+// the cached latent on demand; the WSVD digest ("Method, 3.4") folds the
+// value up-projection into the output side.  The single-pass stream kernel
+// keeps, per workgroup, the absorbed queries Q~ and the running O~ of every
+// head it owns in registers.  At r = 2304 with 40 heads (LLaVA-v1.5-13B) that
+// state is about 550 KB, more than a compute unit holds, so the single pass
+// splits the heads into three workgroups that each stream the cache.  Here the
+// two halves of the work run as two passes that each read the cache once:
+//
+//   wide_scores_kernel  per (sequence, chunk of tokens): S = C Q~^T for every
+//                       head (scores in log2 units, Q~ pre-scaled), written to
+//                       the workspace as S[b][heads][Lp], plus the chunk's
+//                       maximum per head.  Only Q~ is resident.
+//   wide_values_kernel  per (sequence, split, 256-column chunk of r):
+//                       p = 2^(S - m_split), O~ = p^T C over the split's
+//                       tokens for every head and the chunk's columns, and
+//                       l = sum p.  Only a 256-column slice of O~ is resident.
+//
+// The value pass writes (O~ / l, m, l) in the single pass's partial layout, so
+// the log-sum-exp merge and the W^u_v projection that follow are shared.
+#include "device_common.h"
+#include "qsvd_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+namespace qsvd {
+namespace {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWideW = 8;        // wavefronts of the score pass; r = 8 * 32 * NKB
+constexpr int kWideT = 32;       // tokens per tile (both passes)
+constexpr int kWideCW = 256;     // columns per value-pass workgroup
+constexpr int kWideVW = 4;       // wavefronts of the value pass (64 columns each)
+constexpr int kWideCUs = 256;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false)));
+}
+// maximum over each aligned group of 32 lanes
+__device__ __forceinline__ float max32(float v) {
+  v = dpp_max<0xB1>(v);
+  v = dpp_max<0x4E>(v);
+  v = dpp_max<0x141>(v);
+  v = dpp_max<0x140>(v);
+  return fmaxf(v, __shfl_xor(v, 16, kWave));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(n), 0x00020000);
+}
+
+__device__ __forceinline__ int xcd_task() {
+  const int total = gridDim.x, id = blockIdx.x;
+  const int per = total / 8, rem = total % 8, xcd = id % 8, local = id / 8;
+  return xcd * per + min(xcd, rem) + local;
+}
+
+__device__ __forceinline__ bf16x4 wide_read_tr16(const uint8_t *p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16 *)(
+          reinterpret_cast<__attribute__((address_space(3))) uint8_t *>(reinterpret_cast<uintptr_t>(p))));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// ------------------------------------------------------------------ score pass
+// Workgroup (sequence, chunk of C1 tokens), 8 wavefronts; wavefront w owns
+// latent columns 32 NKB w .. +32 NKB.  Per 32-token tile: each wavefront's
+// partial scores S_w = C[:, cols_w] Q~[:, cols_w]^T (v_mfma_f32_16x16x32_bf16,
+// the cache rows straight from the load registers as the A operand, Q~ held
+// as the B operand for the whole chunk) go to LDS; the workgroup sums the 8
+// partials, writes S and keeps the running maximum of each head.
+template <int NH, int NKB>
+__global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
+  constexpr int HS = NH * 16, SPR = kWideT + 4, RW = 32 * NKB;
+  extern __shared__ __attribute__((aligned(16))) float spart[];   // [8][HS][SPR]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int task = xcd_task();
+  const int chunk = task % p.nchunk1;
+  const int64_t seq = task / p.nchunk1;
+  const int64_t L = p.L;
+  const int64_t t_begin = static_cast<int64_t>(chunk) * p.chunk1;
+  const int64_t t_end = std::min<int64_t>(t_begin + p.chunk1, L);
+  const int ntiles = t_begin < t_end ? static_cast<int>((t_end - t_begin + kWideT - 1) / kWideT) : 0;
+  const int64_t row_bytes = static_cast<int64_t>(p.r) * 2;
+  const int j0w = wave * RW;
+  const uint8_t *C = static_cast<const uint8_t *>(p.C);
+
+  // tile registers: [16-token block][K block]: token 16 tb + li, columns
+  // j0w + 32 kb + 8 lg .. +8; a block's rows of the next tile are requested
+  // as soon as its products have read them
+  u32x4 stage[2][NKB];
+  auto load_rows = [&](int it, int tb) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
+    const __amdgpu_buffer_rsrc_t rc = wide_rsrc(C + (seq * L + t0) * row_bytes, (t_end - t0) * row_bytes);
+    const uint32_t vo = static_cast<uint32_t>((16 * tb + li) * row_bytes + (j0w + 8 * lg) * 2);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) stage[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(rc, vo + 64 * kb, 0, 0);
+  };
+  if (ntiles > 0) {
+    load_rows(0, 0);
+    load_rows(0, 1);
+  }
+
+  // absorbed queries as the B operand: head 16 hb + li, columns j0w + 32 kb + 8 lg .. +8
+  bf16x8 qf[NH][NKB];
+  const uint16_t *qt = static_cast<const uint16_t *>(p.qt);
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int h = hb * 16 + li;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (h < p.heads) v = *reinterpret_cast<const u32x4 *>(qt + (seq * p.heads + h) * p.r + j0w + 32 * kb + 8 * lg);
+      qf[hb][kb] = __builtin_bit_cast(bf16x8, v);
+    }
+
+  // the (head, token) items of the cross-wavefront sum: item tid + 512 k is
+  // head tid / 32 + 16 k, token tid % 32 (32 lanes per head)
+  float mrun[NH];
+#pragma unroll
+  for (int k = 0; k < NH; ++k) mrun[k] = -INFINITY;
+  float *S = p.S;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f32x4 sacc[NH];
+#pragma unroll
+      for (int hb = 0; hb < NH; ++hb) sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hb = 0; hb < NH; ++hb)
+          sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, stage[tb][kb]),
+                                                             qf[hb][kb], sacc[hb], 0, 0, 0);
+      if (it + 1 < ntiles) load_rows(it + 1, tb);
+      // lane holds tokens 16 tb + 4 lg + (0..3) of head 16 hb + li
+#pragma unroll
+      for (int hb = 0; hb < NH; ++hb)
+        *reinterpret_cast<f32x4 *>(spart + (wave * HS + hb * 16 + li) * SPR + tb * 16 + 4 * lg) = sacc[hb];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      const int h = (tid >> 5) + 16 * k, t = tid & 31;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWideW; ++w) s += spart[(w * HS + h) * SPR + t];
+      const int64_t tok = t0 + t;
+      if (h < p.heads && tok < t_end) {
+        S[(seq * p.heads + h) * p.Lp + tok] = s;
+        mrun[k] = fmaxf(mrun[k], s);
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    const int h = (tid >> 5) + 16 * k;
+    const float m = max32(mrun[k]);
+    if ((tid & 31) == 0 && h < p.heads) p.m1[(seq * p.nchunk1 + chunk) * p.heads + h] = m;
+  }
+}
+
+// ------------------------------------------------------------------ value pass
+// Workgroup (sequence, split, 256-column chunk cc), 4 wavefronts of 64
+// columns each.  The split's maximum per head comes from the score pass's
+// chunk maxima.  Per 32-token tile, double-buffered in LDS: the tile's
+// 256 columns are loaded by the workgroup one tile ahead (16-byte rows), and
+// each wavefront forms O~^T[cols][heads] += C_tile^T P^T with
+// v_mfma_f32_16x16x32_bf16: A = C^T read by gfx950's transposing LDS loads,
+// B = P^T with p = 2^(S - m) for the lane's head and 8 tokens.
+// workgroups of the value pass per compute unit (its register budget)
+constexpr int wide_values_per_cu(int nh) { return nh <= 3 ? 3 : 2; }
+
+template <int NH>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(wide_values_per_cu(NH), wide_values_per_cu(NH))))
+void wide_values_kernel(WideArgs p) {
+  constexpr int RS = kWideCW * 2 + 16;   // LDS row stride (bytes) of a tile
+  constexpr int NJB = kWideCW / kWideVW / 16;   // 16-column blocks per wavefront
+  __shared__ __attribute__((aligned(16))) uint8_t ct[2][kWideT * RS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int ncc = p.r / kWideCW;
+  const int task = xcd_task();
+  const int cc = task % ncc;
+  const int split = (task / ncc) % p.splits;
+  const int64_t seq = task / (ncc * p.splits);
+  const int64_t L = p.L;
+  const int64_t t_begin = static_cast<int64_t>(split) * p.chunk3;
+  const int64_t t_end = std::min<int64_t>(t_begin + p.chunk3, L);
+  const int ntiles = t_begin < t_end ? static_cast<int>((t_end - t_begin + kWideT - 1) / kWideT) : 0;
+  const int64_t row_bytes = static_cast<int64_t>(p.r) * 2;
+  const uint8_t *C = static_cast<const uint8_t *>(p.C);
+
+  // the split's reference maximum for this lane's heads 16 hb + li: the
+  // maximum over the score-pass chunks the split overlaps (an upper bound of
+  // the split's own maximum, which the merge's rescaling accepts)
+  float mh[NH];
+  {
+    const int c0 = static_cast<int>(t_begin / p.chunk1);
+    const int c1 = std::min(static_cast<int>((t_end + p.chunk1 - 1) / p.chunk1), p.nchunk1);
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+      const int h = hb * 16 + li;
+      float m = -INFINITY;
+      if (h < p.heads)
+        for (int c = c0; c < c1; ++c) m = fmaxf(m, p.m1[(seq * p.nchunk1 + c) * p.heads + h]);
+      mh[hb] = m;
+    }
+  }
+
+  // tile loads: 16-byte chunk q = tid + 256 k is row q / 32, columns 8 (q % 32) .. +8
+  u32x4 stage[4];
+  auto load_tile = [&](int it) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
+    const __amdgpu_buffer_rsrc_t rc = wide_rsrc(C + (seq * L + t0) * row_bytes, (t_end - t0) * row_bytes);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = tid + 256 * k;
+      stage[k] = __builtin_amdgcn_raw_buffer_load_b128(
+          rc, static_cast<uint32_t>((q >> 5) * row_bytes + cc * kWideCW * 2 + (q & 31) * 16), 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = tid + 256 * k;
+      *reinterpret_cast<u32x4 *>(&ct[buf][(q >> 5) * RS + (q & 31) * 16]) = stage[k];
+    }
+  };
+
+  f32x4 oacc[NH][NJB];
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) oacc[hb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum[NH];
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb) lsum[hb] = 0.f;
+
+  // scores of this lane's heads and tokens t0 + 8 lg + (0..7), one tile ahead
+  f32x4 sv[NH][2];
+  auto load_scores = [&](int it) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+      const int h = min(hb * 16 + li, p.heads - 1);   // padded heads read a real row, unused
+      const float *src = p.S + (seq * p.heads + h) * p.Lp + t0 + 8 * lg;
+      sv[hb][0] = *reinterpret_cast<const f32x4 *>(src);
+      sv[hb][1] = *reinterpret_cast<const f32x4 *>(src + 4);
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    load_scores(0);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
+    store_tile(buf);
+    f32x4 scur[NH][2];
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+      scur[hb][0] = sv[hb][0];
+      scur[hb][1] = sv[hb][1];
+    }
+    __syncthreads();   // the tile is in LDS; the other buffer's readers are done
+    if (it + 1 < ntiles) {
+      load_tile(it + 1);
+      load_scores(it + 1);
+    }
+
+    // P^T: head 16 hb + li, tokens t0 + 8 lg + (0..7)
+    bf16x8 pb[NH];
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+      const int h = hb * 16 + li;
+      float pe[8];
+      if (h < p.heads) {
+        const f32x4 a = scur[hb][0], b = scur[hb][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pe[e] = t0 + 8 * lg + e < t_end ? __builtin_amdgcn_exp2f(a[e] - mh[hb]) : 0.f;
+          pe[4 + e] = t0 + 8 * lg + 4 + e < t_end ? __builtin_amdgcn_exp2f(b[e] - mh[hb]) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = 0.f;
+      }
+      typedef float f32x8 __attribute__((ext_vector_type(8)));
+      const bf16x8 pv = __builtin_convertvector(f32x8{pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]}, bf16x8);
+      pb[hb] = pv;
+      // l sums the same bf16 probabilities the product uses
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lsum[hb] += static_cast<float>(pv[e]);
+    }
+
+    // A = C^T: column 16 jb + li of this wavefront, tokens 8 lg + (0..7)
+    const uint8_t *trb = &ct[buf][(8 * lg + (li >> 2)) * RS + (wave * (kWideCW / kWideVW) + 4 * (li & 3)) * 2];
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      const bf16x4 lo = wide_read_tr16(trb + jb * 32);
+      const bf16x4 hi = wide_read_tr16(trb + 4 * RS + jb * 32);
+      const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int hb = 0; hb < NH; ++hb)
+        oacc[hb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hb], oacc[hb][jb], 0, 0, 0);
+    }
+  }
+
+  // l per head: the 4 lane groups hold disjoint tokens
+  const int nsplit = p.splits;
+  const int rw = kWideCW / kWideVW;
+  const int cg = cc * kWideVW + wave;   // 64-column group of r
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb) {
+    float l = lsum[hb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int h = hb * 16 + li;
+    if (h >= p.heads) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // oacc[hb][jb] element e: column 16 jb + 4 lg + e of the wavefront's group, head h
+    uint16_t *dst = p.opart + (((seq * nsplit + split) * (p.r / rw) + cg) * p.heads + h) * rw;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+      *reinterpret_cast<u32x2 *>(dst + jb * 16 + 4 * lg) =
+          u32x2{pack_bf16x2(oacc[hb][jb][0] * inv, oacc[hb][jb][1] * inv),
+                pack_bf16x2(oacc[hb][jb][2] * inv, oacc[hb][jb][3] * inv)};
+    if (cc == 0 && wave == 0 && lg == 0) {
+      p.ml[2 * ((seq * nsplit + split) * p.heads + h)] = mh[hb];
+      p.ml[2 * ((seq * nsplit + split) * p.heads + h) + 1] = l;
+    }
+  }
+}
+
+template <int NH, int NKB>
+hipError_t launch_scores_t(const WideArgs &a, hipStream_t s) {
+  auto kern = wide_scores_kernel<NH, NKB>;
+  const size_t lds = static_cast<size_t>(kWideW) * NH * 16 * (kWideT + 4) * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  kern<<<dim3(static_cast<unsigned>(a.b * a.nchunk1)), dim3(64 * kWideW), lds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int NH>
+hipError_t launch_scores_nh(const WideArgs &a, int nkb, hipStream_t s) {
+  switch (nkb) {
+    case 7: return launch_scores_t<NH, 7>(a, s);
+    case 8: return launch_scores_t<NH, 8>(a, s);
+    default: return launch_scores_t<NH, 9>(a, s);
+  }
+}
+
+}  // namespace
+
+// Two passes when the single pass would split the heads into three or more
+// workgroups: bf16 cache, r = 8 * 32 * NKB with 7 <= NKB <= 9 (up to r = 2304)
+// and 33..64 heads (3 or 4 blocks of 16; Q~ of all heads fits the registers).
+bool wide_applies(int r, int heads, int c_dtype, int head_groups) {
+  if (c_dtype != QSVD_BF16 || head_groups < 3) return false;
+  if (r % (kWideW * 32) != 0 || r % kWideCW != 0) return false;
+  const int nkb = r / (kWideW * 32);
+  return nkb >= 7 && nkb <= 9 && heads > 32 && heads <= 64;
+}
+
+void wide_plan(int b, int64_t L, int r, int heads, WidePlanInfo *w) {
+  const int64_t tiles = (L + kWideT - 1) / kWideT;
+  // score pass: one workgroup per compute unit
+  int64_t nchunk = std::max<int64_t>(1, (kWideCUs + b - 1) / b);
+  nchunk = std::min<int64_t>(nchunk, tiles);
+  const int64_t chunk1 = ((tiles + nchunk - 1) / nchunk) * kWideT;
+  nchunk = (L + chunk1 - 1) / chunk1;
+  // value pass: as many splits as one round of workgroups holds, each a whole
+  // number of tiles
+  const int64_t slots = static_cast<int64_t>(kWideCUs) * wide_values_per_cu((heads + 15) / 16);
+  int64_t splits = std::max<int64_t>(1, slots / (static_cast<int64_t>(b) * (r / kWideCW)));
+  splits = std::min<int64_t>(std::min<int64_t>(splits, tiles), 1024);
+  const int64_t chunk3 = ((tiles + splits - 1) / splits) * kWideT;
+  w->chunk1 = chunk1;
+  w->nchunk1 = static_cast<int>(nchunk);
+  w->chunk3 = chunk3;
+  w->splits = static_cast<int>((L + chunk3 - 1) / chunk3);
+  w->Lp = ((L + kWideT - 1) / kWideT) * kWideT;
+  w->s_bytes = static_cast<size_t>(b) * heads * w->Lp * sizeof(float);
+  w->m1_bytes = static_cast<size_t>(b) * w->nchunk1 * heads * sizeof(float);
+  w->rw = kWideCW / kWideVW;
+}
+
+hipError_t launch_wide_scores(const WideArgs &a, hipStream_t s) {
+  const int nh = (a.heads + 15) / 16, nkb = a.r / (kWideW * 32);
+  LaunchTimer t("decode_scores", s);
+  return nh == 3 ? launch_scores_nh<3>(a, nkb, s) : launch_scores_nh<4>(a, nkb, s);
+}
+
+hipError_t launch_wide_values(const WideArgs &a, hipStream_t s) {
+  const int nh = (a.heads + 15) / 16;
+  const unsigned grid = static_cast<unsigned>(a.b * a.splits * (a.r / kWideCW));
+  LaunchTimer t("decode_values", s);
+  if (nh == 3)
+    wide_values_kernel<3><<<dim3(grid), dim3(64 * kWideVW), 0, s>>>(a);
+  else
+    wide_values_kernel<4><<<dim3(grid), dim3(64 * kWideVW), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace qsvd

@@ -107,6 +107,33 @@ struct DecodeArgs {
   void *workspace;
 };
 
+// Two-pass decode for wide latents with many heads (bf16 caches): a score pass
+// writes S[b][heads][Lp] and per-chunk maxima; a value pass writes the split
+// partials in the single pass's layout for the shared merge.
+struct WideArgs {
+  const void *C;          // [b][L][r] bf16
+  const uint16_t *qt;     // absorbed queries [b][heads][r]
+  float *S;               // [b][heads][Lp]
+  float *m1;              // [b][nchunk1][heads]
+  uint16_t *opart;        // [b][splits][r / 64][heads][64]
+  float *ml;              // [b][splits][heads][2]
+  int64_t L, Lp, chunk1, chunk3;
+  int b, r, heads, nchunk1, splits;
+};
+
+struct WidePlanInfo {
+  int64_t chunk1;   // tokens per score-pass workgroup (multiple of 32)
+  int64_t chunk3;   // tokens per value-pass split (multiple of 32)
+  int64_t Lp;       // L rounded up to 32
+  int nchunk1, splits, rw;
+  size_t s_bytes, m1_bytes;
+};
+
+bool wide_applies(int r, int heads, int c_dtype, int head_groups);
+void wide_plan(int b, int64_t L, int r, int heads, WidePlanInfo *w);
+hipError_t launch_wide_scores(const WideArgs &a, hipStream_t s);
+hipError_t launch_wide_values(const WideArgs &a, hipStream_t s);
+
 // Shape of the MFMA stream kernel: W wavefronts of RW = 32 NKB latent columns
 // each (r = W RW), NHB 16-head blocks per workgroup, T tokens per tile.
 struct MfmaShape {
@@ -125,6 +152,9 @@ struct DecodePlan {
   int head_groups;   // workgroups per (sequence, split) along heads
   int group_heads;   // heads per head group
   bool mfma;         // bf16 / quantised MFMA stream kernel (else float32 kernel)
+  bool wide;         // two-pass decode (score pass + value pass) instead of the stream kernel
+  WidePlanInfo wp;   // its chunking (wide only)
+  int rw;            // columns per partial block of the split partials
   size_t qt_bytes;   // absorbed queries
   size_t part_bytes; // per-split partial state
   size_t total;

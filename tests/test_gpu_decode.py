@@ -180,3 +180,27 @@ def test_output_unchanged_by_rotation_on_gpu():
     b = synth.decode_case(1024, 8, 128, 512, 2, 256, dtype="bf16", hadamard=0, seed=3)
     ga, gb = decode_case_on_gpu(a), decode_case_on_gpu(b)
     assert oracle.rel_l2(ga, gb) <= TOL_BF16
+
+
+# ------------------------------------------------------------------ two-pass decode
+WIDE_SHAPES = [
+    # heads, r, b, L: bf16 caches whose single pass would need 3 or more head groups
+    (40, 2304, 2, 1000),     # the 13B geometry, ragged chunks
+    (36, 1792, 3, 77),       # one partial chunk per sequence
+    (64, 2048, 1, 4097),     # four 16-head blocks, one token past a tile
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: "h{}r{}b{}L{}".format(*s))
+def test_two_pass_decode(shape):
+    """Score pass + value pass + the shared merge against the explicit-K/V oracle."""
+    heads, r, b, L = shape
+    say(f"case: two-pass decode heads={heads} r={r} b={b} L={L}")
+    cs = synth.decode_case(heads * 128, heads, 128, r, b, L, dtype="bf16", hadamard=128, seed=heads + L)
+    got = decode_case_on_gpu(cs)
+    assert np.all(np.isfinite(got))
+    err = oracle.rel_l2(got, oracle_out(cs))
+    say(f"  rel-L2 {err:.2e}")
+    assert err <= TOL_BF16
+    # the result does not depend on the split argument (the two passes choose their own chunks)
+    assert np.array_equal(decode_case_on_gpu(cs, splits=5), got)
