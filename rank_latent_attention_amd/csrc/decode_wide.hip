@@ -190,7 +190,9 @@ template <int NH>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(wide_values_per_cu(NH), wide_values_per_cu(NH))))
 void wide_values_kernel(WideArgs p) {
-  constexpr int RS = kWideCW * 2 + 16;   // LDS row stride (bytes) of a tile
+  // LDS row stride of a tile: 32 bytes of padding move each row 8 banks, so
+  // the 4 rows of a transposing read land in distinct banks
+  constexpr int RS = kWideCW * 2 + 32;
   constexpr int NJB = kWideCW / kWideVW / 16;   // 16-column blocks per wavefront
   __shared__ __attribute__((aligned(16))) uint8_t ct[2][kWideT * RS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -297,8 +299,14 @@ void wide_values_kernel(WideArgs p) {
         const f32x4 a = scur[hb][0], b = scur[hb][1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pe[e] = t0 + 8 * lg + e < t_end ? __builtin_amdgcn_exp2f(a[e] - mh[hb]) : 0.f;
-          pe[4 + e] = t0 + 8 * lg + 4 + e < t_end ? __builtin_amdgcn_exp2f(b[e] - mh[hb]) : 0.f;
+          pe[e] = __builtin_amdgcn_exp2f(a[e] - mh[hb]);
+          pe[4 + e] = __builtin_amdgcn_exp2f(b[e] - mh[hb]);
+        }
+        if (t0 + kWideT > t_end) {   // the partial last tile: tokens past the split drop out
+          const int valid = static_cast<int>(t_end - t0) - 8 * lg;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= valid) pe[e] = 0.f;
         }
       } else {
 #pragma unroll
