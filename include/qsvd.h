@@ -148,6 +148,11 @@ qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int
  *            float32 per-column scales wu_scale_k / wu_scale_v [E], else NULL.
  *   O        [b][heads][d]        F32 or BF16 (o_dtype)
  *   splits   number of L-splits per sequence; 0 lets the library choose.
+ *            BF16 caches with 33..64 heads and r = 256 k (7 <= k <= 9), whose
+ *            per-head state would not fit one workgroup, run as two passes
+ *            (all-head scores to the workspace, then the value product per
+ *            256-column chunk); they choose their own chunking and ignore
+ *            splits.
  *   workspace   device scratch of at least qsvd_decode_workspace_bytes(...)
  *            bytes (same b, L, r, heads, d, c_dtype and splits).
  *
