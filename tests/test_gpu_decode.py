@@ -188,6 +188,8 @@ WIDE_SHAPES = [
     (40, 2304, 2, 1000),     # the 13B geometry, ragged chunks
     (36, 1792, 3, 77),       # one partial chunk per sequence
     (64, 2048, 1, 4097),     # four 16-head blocks, one token past a tile
+    (33, 2048, 1, 5),        # one valid head in the last block, fewer tokens than a tile
+    (48, 2304, 5, 300),      # an odd batch, ragged tiles
 ]
 
 
