@@ -206,3 +206,17 @@ def test_two_pass_decode(shape):
     assert err <= TOL_BF16
     # the result does not depend on the split argument (the two passes choose their own chunks)
     assert np.array_equal(decode_case_on_gpu(cs, splits=5), got)
+
+
+@pytest.mark.parametrize("factor", [30.0, 300.0])
+def test_two_pass_sharpened_softmax(factor):
+    """Peaked attention through the two passes: the value pass's reference
+    maximum (over the score chunks a split overlaps) and the merge rescaling."""
+    say(f"case: two-pass sharpened x{factor}")
+    cs = synth.decode_case(40 * 128, 40, 128, 2304, 2, 1500, dtype="bf16", hadamard=128, p=0.5, seed=78)
+    qv = synth.to_bf16_bits(synth.sharpen_query(values(cs.q, "bf16"), factor))
+    ref = oracle_out(cs, qv=values(qv, "bf16"))
+    got = decode_case_on_gpu(cs, q_override=qv)
+    err = oracle.rel_l2(got, ref)
+    say(f"  rel-L2 {err:.2e}")
+    assert err <= TOL_BF16

@@ -142,3 +142,19 @@ def test_headwise_longer_rope_tables():
                                 0, O, q.F32, ws)
     torch.cuda.synchronize()
     assert np.array_equal(host(O), want)
+
+
+@pytest.mark.parametrize("factor", [10.0, 60.0])
+def test_headwise_sharpened_softmax(factor):
+    """Peaked attention (a few tokens carry most of the weight) with RoPE and
+    several splits: the online rescaling and the merge."""
+    cs = synth.headwise_case(2, 900, 8, 128, 64, 64, seed=44)
+    qs = np.ascontiguousarray(synth.to_bf16_bits(values(cs.q, "bf16") * factor))
+    import dataclasses
+    cs = dataclasses.replace(cs, q=qs)
+    say(f"case: headwise sharpened x{factor}")
+    for splits in (0, 5):
+        got = run_headwise(cs, rope=True, splits=splits)
+        err = oracle.rel_l2(got, oracle_out(cs, True))
+        say(f"  splits={splits} rel-L2 {err:.2e}")
+        assert err <= TOL
