@@ -178,23 +178,38 @@ __global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
 // ------------------------------------------------------------------ value pass
 // Workgroup (sequence, split, 256-column chunk cc), 4 wavefronts of 64
 // columns each.  The split's maximum per head comes from the score pass's
-// chunk maxima.  Per 32-token tile, double-buffered in LDS: the tile's
-// 256 columns are loaded by the workgroup one tile ahead (16-byte rows), and
-// each wavefront forms O~^T[cols][heads] += C_tile^T P^T with
-// v_mfma_f32_16x16x32_bf16: A = C^T read by gfx950's transposing LDS loads,
-// B = P^T with p = 2^(S - m) for the lane's head and 8 tokens.
+// chunk maxima.  A 32-token tile (32 rows x 512 bytes) moves from memory
+// straight into an LDS buffer by buffer_load ... lds, NBUF - 1 tiles ahead of
+// the one in use; in LDS the 16-byte chunk c of row R sits at c ^ vsw(R), so
+// the 4 rows of a transposing read fall in distinct banks.  The probabilities
+// p = 2^(S - m) of a tile are formed once per workgroup, one tile ahead
+// (wavefront w: tokens 8 w .. 8 w + 7 of every head), as bf16 MFMA operand
+// fragments in LDS.  Each wavefront forms O~^T[cols][heads] += C_tile^T P^T
+// with v_mfma_f32_16x16x32_bf16: A = C^T from gfx950's transposing LDS reads,
+// B = P^T from the fragments.
+__device__ __forceinline__ int vsw(int row) { return 2 * (row & 3); }
+
 // workgroups of the value pass per compute unit (its register budget)
 constexpr int wide_values_per_cu(int nh) { return nh <= 3 ? 3 : 2; }
+// LDS tile buffers: as many as that many workgroups hold beside the p fragments
+constexpr int wide_values_bufs(int nh) { return nh <= 3 ? 2 : 3; }
 
 template <int NH>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(wide_values_per_cu(NH), wide_values_per_cu(NH))))
 void wide_values_kernel(WideArgs p) {
-  // LDS row stride of a tile: 32 bytes of padding move each row 8 banks, so
-  // the 4 rows of a transposing read land in distinct banks
-  constexpr int RS = kWideCW * 2 + 32;
+  constexpr int RB = kWideCW * 2;               // bytes of a tile row
+  constexpr int TB = kWideT * RB;               // bytes of a tile
   constexpr int NJB = kWideCW / kWideVW / 16;   // 16-column blocks per wavefront
-  __shared__ __attribute__((aligned(16))) uint8_t ct[2][kWideT * RS];
+  constexpr int NBUF = wide_values_bufs(NH);
+  constexpr int PB = NH * 64 * 16;              // bytes of a tile's p fragments
+  // vmcnt once a tile's DMA has landed: the loads issued after it are the
+  // next tiles' score loads (NH) and DMA (4), NBUF - 2 groups of them
+  constexpr int kAfter = (NBUF - 2) * (NH + 4);
+  constexpr int kWaitImm = (kAfter & 15) | ((kAfter >> 4) << 14) | 0x0070 | 0x0F00;
+  __shared__ __attribute__((aligned(1024))) uint8_t ct[NBUF][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t pf[2][PB];
+  __shared__ float lred[kWideVW][NH * 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -227,23 +242,50 @@ void wide_values_kernel(WideArgs p) {
     }
   }
 
-  // tile loads: 16-byte chunk q = tid + 256 k is row q / 32, columns 8 (q % 32) .. +8
-  u32x4 stage[4];
-  auto load_tile = [&](int it) {
+  // DMA of tile it into buffer buf: wavefront w fills rows 8 w .. 8 w + 7, two
+  // rows per instruction (lane l: row 2 m + l / 32, LDS chunk l % 32)
+  auto dma_tile = [&](int it, int buf) {
     const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
     const __amdgpu_buffer_rsrc_t rc = wide_rsrc(C + (seq * L + t0) * row_bytes, (t_end - t0) * row_bytes);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int q = tid + 256 * k;
-      stage[k] = __builtin_amdgcn_raw_buffer_load_b128(
-          rc, static_cast<uint32_t>((q >> 5) * row_bytes + cc * kWideCW * 2 + (q & 31) * 16), 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int m = wave * 4 + i;
+      const int row = 2 * m + (lane >> 5);
+      const uint32_t vo = static_cast<uint32_t>(row * row_bytes + cc * RB + (((lane & 31) ^ vsw(row)) * 16));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rc, (__attribute__((address_space(3))) void *)(&ct[buf][2 * m * RB]), 16, vo, 0, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+  // scores of this lane's heads 16 hb + li and tokens t0 + 8 wave + 2 lg + (0, 1)
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  auto load_scores = [&](int it, f32x2 (&dst)[NH]) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int q = tid + 256 * k;
-      *reinterpret_cast<u32x4 *>(&ct[buf][(q >> 5) * RS + (q & 31) * 16]) = stage[k];
+    for (int hb = 0; hb < NH; ++hb) {
+      const int h = min(hb * 16 + li, p.heads - 1);   // padded heads read a real row, unused
+      dst[hb] = *reinterpret_cast<const f32x2 *>(p.S + (seq * p.heads + h) * p.Lp + t0 + 8 * wave + 2 * lg);
+    }
+  };
+  // p of tile it from its scores into fragment buffer pbuf: the fragment of
+  // lane (li, g) of head block hb holds tokens 8 g .. 8 g + 7 of head 16 hb + li
+  float lsum[NH];
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb) lsum[hb] = 0.f;
+  auto make_p = [&](int it, const f32x2 (&sv)[NH], int pbuf, bool count) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
+    const int64_t tk = t0 + 8 * wave + 2 * lg;
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+      const int h = hb * 16 + li;
+      float p0 = __builtin_amdgcn_exp2f(sv[hb][0] - mh[hb]);
+      float p1 = __builtin_amdgcn_exp2f(sv[hb][1] - mh[hb]);
+      if (h >= p.heads || tk >= t_end) p0 = 0.f;   // tokens past the split drop out
+      if (h >= p.heads || tk + 1 >= t_end) p1 = 0.f;
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+      *reinterpret_cast<uint32_t *>(&pf[pbuf][(hb * 64 + wave * 16 + li) * 16 + 4 * lg]) = pk;
+      // l sums the same bf16 probabilities the product uses
+      if (count) lsum[hb] += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xFFFF0000u);
     }
   };
 
@@ -252,97 +294,79 @@ void wide_values_kernel(WideArgs p) {
   for (int hb = 0; hb < NH; ++hb)
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[hb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lsum[NH];
-#pragma unroll
-  for (int hb = 0; hb < NH; ++hb) lsum[hb] = 0.f;
 
-  // scores of this lane's heads and tokens t0 + 8 lg + (0..7), one tile ahead
-  f32x4 sv[NH][2];
-  auto load_scores = [&](int it) {
-    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
-#pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {
-      const int h = min(hb * 16 + li, p.heads - 1);   // padded heads read a real row, unused
-      const float *src = p.S + (seq * p.heads + h) * p.Lp + t0 + 8 * lg;
-      sv[hb][0] = *reinterpret_cast<const f32x4 *>(src);
-      sv[hb][1] = *reinterpret_cast<const f32x4 *>(src + 4);
-    }
-  };
-
+  // Order of the loads: scores 0, DMA 0, then per tile k the scores of tile
+  // k + 1 and the DMA of tile k + NBUF - 1 (past the end: repeats of the last
+  // tile into a buffer that is not read again), so the count of loads issued
+  // after a tile's DMA is fixed.
+  f32x2 snext[NH];
   if (ntiles > 0) {
-    load_tile(0);
-    load_scores(0);
+    f32x2 s0[NH];
+    load_scores(0, s0);
+    make_p(0, s0, 0, true);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_tile(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_scores(min(1, ntiles - 1), snext);
+    if constexpr (NBUF == 3) dma_tile(min(1, ntiles - 1), 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
-    store_tile(buf);
-    f32x4 scur[NH][2];
+    const int buf = it % NBUF;
+    f32x2 scur[NH];
 #pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {
-      scur[hb][0] = sv[hb][0];
-      scur[hb][1] = sv[hb][1];
-    }
-    __syncthreads();   // the tile is in LDS; the other buffer's readers are done
-    if (it + 1 < ntiles) {
-      load_tile(it + 1);
-      load_scores(it + 1);
-    }
+    for (int hb = 0; hb < NH; ++hb) scur[hb] = snext[hb];
+    // tile it and p(it) are in LDS for every wavefront; every wavefront is
+    // done with tile it - 1 and p(it - 1)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitImm);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_scores(min(it + 2, ntiles - 1), snext);
+    dma_tile(min(it + NBUF - 1, ntiles - 1), (it + NBUF - 1) % NBUF);
+    __builtin_amdgcn_sched_barrier(0);
+    // p of the next tile (a repeat past the end: written, not read, not counted)
+    make_p(min(it + 1, ntiles - 1), scur, (it + 1) & 1, it + 1 < ntiles);
 
-    // P^T: head 16 hb + li, tokens t0 + 8 lg + (0..7)
     bf16x8 pb[NH];
 #pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {
-      const int h = hb * 16 + li;
-      float pe[8];
-      if (h < p.heads) {
-        const f32x4 a = scur[hb][0], b = scur[hb][1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pe[e] = __builtin_amdgcn_exp2f(a[e] - mh[hb]);
-          pe[4 + e] = __builtin_amdgcn_exp2f(b[e] - mh[hb]);
-        }
-        if (t0 + kWideT > t_end) {   // the partial last tile: tokens past the split drop out
-          const int valid = static_cast<int>(t_end - t0) - 8 * lg;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= valid) pe[e] = 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pe[e] = 0.f;
-      }
-      typedef float f32x8 __attribute__((ext_vector_type(8)));
-      const bf16x8 pv = __builtin_convertvector(f32x8{pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]}, bf16x8);
-      pb[hb] = pv;
-      // l sums the same bf16 probabilities the product uses
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lsum[hb] += static_cast<float>(pv[e]);
-    }
+    for (int hb = 0; hb < NH; ++hb) pb[hb] = *reinterpret_cast<const bf16x8 *>(&pf[it & 1][(hb * 64 + lane) * 16]);
 
-    // A = C^T: column 16 jb + li of this wavefront, tokens 8 lg + (0..7)
-    const uint8_t *trb = &ct[buf][(8 * lg + (li >> 2)) * RS + (wave * (kWideCW / kWideVW) + 4 * (li & 3)) * 2];
+    // A = C^T: column 16 jb + li of this wavefront, tokens 8 lg + (0..7): lane
+    // li reads 8 bytes of row 8 lg + li / 4 (+ 4) at column 4 (li % 4)
+    const int rlo = 8 * lg + (li >> 2);
+    const uint8_t *rowp = &ct[buf][rlo * RB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
-      const bf16x4 lo = wide_read_tr16(trb + jb * 32);
-      const bf16x4 hi = wide_read_tr16(trb + 4 * RS + jb * 32);
+      const int ob = wave * (kWideCW / kWideVW) * 2 + jb * 32 + 8 * (li & 3);   // byte within the row
+      const int pos = (((ob >> 4) ^ vsw(rlo)) << 4) | (ob & 15);
+      const bf16x4 lo = wide_read_tr16(rowp + pos);
+      const bf16x4 hi = wide_read_tr16(rowp + 4 * RB + pos);   // rows + 4 share the swizzle
       const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int hb = 0; hb < NH; ++hb)
         oacc[hb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hb], oacc[hb][jb], 0, 0, 0);
     }
   }
+  // the repeated DMAs past the end land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0070);
 
-  // l per head: the 4 lane groups hold disjoint tokens
-  const int nsplit = p.splits;
-  const int rw = kWideCW / kWideVW;
-  const int cg = cc * kWideVW + wave;   // 64-column group of r
+  // l per head: the 4 lane groups and the 4 wavefronts hold disjoint tokens
 #pragma unroll
   for (int hb = 0; hb < NH; ++hb) {
     float l = lsum[hb];
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
+    if (lg == 0) lred[wave][hb * 16 + li] = l;
+  }
+  __syncthreads();
+  const int nsplit = p.splits;
+  const int rw = kWideCW / kWideVW;
+  const int cg = cc * kWideVW + wave;   // 64-column group of r
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb) {
     const int h = hb * 16 + li;
+    const float l = (lred[0][hb * 16 + li] + lred[1][hb * 16 + li]) + (lred[2][hb * 16 + li] + lred[3][hb * 16 + li]);
     if (h >= p.heads) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     // oacc[hb][jb] element e: column 16 jb + 4 lg + e of the wavefront's group, head h
