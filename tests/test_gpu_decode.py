@@ -208,12 +208,14 @@ def test_two_pass_decode(shape):
     assert np.array_equal(decode_case_on_gpu(cs, splits=5), got)
 
 
+@pytest.mark.parametrize("heads,r,L", [(40, 2304, 1500), (64, 2048, 1300)], ids=["h40", "h64"])
 @pytest.mark.parametrize("factor", [30.0, 300.0])
-def test_two_pass_sharpened_softmax(factor):
+def test_two_pass_sharpened_softmax(factor, heads, r, L):
     """Peaked attention through the two passes: the value pass's reference
-    maximum (over the score chunks a split overlaps) and the merge rescaling."""
-    say(f"case: two-pass sharpened x{factor}")
-    cs = synth.decode_case(40 * 128, 40, 128, 2304, 2, 1500, dtype="bf16", hadamard=128, p=0.5, seed=78)
+    maximum (over the score chunks a split overlaps), its tile pipeline (two
+    LDS buffers at 40 heads, three at 64) and the merge rescaling."""
+    say(f"case: two-pass sharpened x{factor} heads={heads} r={r} L={L}")
+    cs = synth.decode_case(heads * 128, heads, 128, r, 2, L, dtype="bf16", hadamard=128, p=0.5, seed=78)
     qv = synth.to_bf16_bits(synth.sharpen_query(values(cs.q, "bf16"), factor))
     ref = oracle_out(cs, qv=values(qv, "bf16"))
     got = decode_case_on_gpu(cs, q_override=qv)
