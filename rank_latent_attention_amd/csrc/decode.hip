@@ -558,7 +558,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       for (int hb = 0; hb < NHB; ++hb)
         *reinterpret_cast<f32x4 *>(spart + (wave * HGP + hb * 16 + li) * SPR + tb * 16 + 4 * lg) = sacc[hb];
     }
-    __syncthreads();
+    lds_barrier();   // the next tile's loads stay in flight
 
     // ---- 4. cross-wavefront sum + online softmax; T/2 lanes per head, 2 tokens each
     for (int item = tid; item < HGP * (T / 2); item += nthreads) {
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       uint16_t *pdst = pl + ((ks * NHB + (h >> 4)) * 64 + 16 * (tk / PPL) + (h & 15)) * PPL + (tk % PPL);
       *reinterpret_cast<uint32_t *>(pdst) = pp;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 5. O~^T = O~^T * alpha + C_tile^T P^T (the rescale is skipped by a
     // wavefront whose heads all kept their running maximum)

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
       for (int hb = 0; hb < NH; ++hb)
         *reinterpret_cast<f32x4 *>(spart + (wave * HS + hb * 16 + li) * SPR + tb * 16 + 4 * lg) = sacc[hb];
     }
-    __syncthreads();
+    lds_barrier();   // the next tile's loads stay in flight
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       const int h = (tid >> 5) + 16 * k, t = tid & 31;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
         mrun[k] = fmaxf(mrun[k], s);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
 #pragma unroll
@@ -320,7 +320,7 @@ void wide_values_kernel(WideArgs p) {
     // done with tile it - 1 and p(it - 1)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitImm);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();   // also completes this wavefront's p fragment writes first
     __builtin_amdgcn_sched_barrier(0);
     load_scores(min(it + 2, ntiles - 1), snext);
     dma_tile(min(it + NBUF - 1, ntiles - 1), (it + NBUF - 1) % NBUF);

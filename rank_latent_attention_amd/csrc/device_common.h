@@ -19,6 +19,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Workgroup barrier that orders LDS only: this wavefront's LDS accesses before
+// it complete first and none moves across it.  Global loads in flight stay in
+// flight (the fence of __syncthreads waits for every outstanding global load,
+// which turns a prefetch issued before the barrier into a synchronous read).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
