@@ -688,11 +688,12 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
             u32x2{cvt_bf16x2(oacc[hb][jb][0] * inv, oacc[hb][jb][1] * inv),
                   cvt_bf16x2(oacc[hb][jb][2] * inv, oacc[hb][jb][3] * inv)};
     }
-    // same-wavefront LDS write -> read, ordered by the LDS queue
+    // same-wavefront LDS write -> read, ordered by the LDS queue; the partials
+    // stream out with non-temporal stores (written once, read once by the merge)
     uint16_t *dst = p.opart + ((static_cast<int64_t>(seq) * p.S + split) * W + wave) *
                                   static_cast<int64_t>(p.heads) * RW + static_cast<int64_t>(h0) * RW;
     for (int u = lane; u < hg * RW / 8; u += 64)
-      *reinterpret_cast<u32x4 *>(dst + u * 8) = *reinterpret_cast<const u32x4 *>(ot + u * 8);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(ot + u * 8), reinterpret_cast<u32x4 *>(dst + u * 8));
   }
   for (int h = tid; h < hg; h += nthreads) {
     p.ml[2 * (pbase + h)] = m_s[h];

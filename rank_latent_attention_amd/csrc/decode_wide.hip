@@ -160,7 +160,7 @@ __global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
       for (int w = 0; w < kWideW; ++w) s += spart[(w * HS + h) * SPR + t];
       const int64_t tok = t0 + t;
       if (h < p.heads && tok < t_end) {
-        S[(seq * p.heads + h) * p.Lp + tok] = s;
+        __builtin_nontemporal_store(s, &S[(seq * p.heads + h) * p.Lp + tok]);   // streamed out, read by the value pass
         mrun[k] = fmaxf(mrun[k], s);
       }
     }
