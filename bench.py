@@ -14,6 +14,11 @@ head caches rk = 64 key and rv = 64 value latents per token; keys rebuilt on
 chip with RoPE, B_Vh applied after the softmax; qsvd_decode_attn_headwise),
 against the HBM peak.
 
+Other decode configurations: the W8A4 shape (int4 group-128 latent cache,
+r = 768, int8 W^u) and the LLaVA-v1.5-13B shape (r = 2304, 40 heads, b = 8,
+L = 16384, bf16 cache; two-pass stream), each with its stream kernels priced
+against the HBM peak.
+
 Prefill leg: the shared down-projection at W8A8, X [16384][4096] int8 (H1
 rotated, per-token scales) times W^d [4096][1536] int8 (per-column scales),
 reported as TOPS; plus the rotate+quantise steps around it.
@@ -61,6 +66,8 @@ def parse():
                     help="skip the explicit K/V reconstruction (RoPE) decode leg")
     ap.add_argument("--no-headwise", action="store_true",
                     help="skip the per-head latent (RoPE) decode leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the W8A4 (int4 cache) and 13B (two-pass) decode legs")
     return ap.parse_args()
 
 
@@ -115,6 +122,7 @@ def main():
     log(f"[bench] generated decode inputs ({cfg.name}) in {time.time() - t0:.1f}s")
     C0 = bf(cs.C)
     copies = [C0] + [C0.clone() for _ in range(max(args.copies, 1) - 1)]
+    n_copies = len(copies)
     qv, Wk, Wv = bf(cs.q), bf(cs.Wu_k), bf(cs.Wu_v)
     O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
     ws_bytes = q.qsvd_decode_workspace_bytes(b, L, r, heads, d, q.BF16, args.splits)
@@ -192,6 +200,13 @@ def main():
     if not args.no_headwise:
         headwise = headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args)
 
+    # ------------------------------------------------------------------ other decode configurations
+    configs = None
+    if not args.no_configs:
+        del copies, C0
+        configs = {"w8a4_int4_cache": w8a4_leg(q, torch, np, synth, dev, bf, args),
+                   "llava13b_two_pass": llava13b_leg(q, torch, synth, bf, args)}
+
     # ------------------------------------------------------------------ prefill
     prefill = None
     if not args.no_prefill:
@@ -260,7 +275,7 @@ def main():
         "config": {"workload": "latent-attention decode step, E=4096 (32x128), r=1536, b=16, "
                                "L=8192, bf16 latent cache (LLaVA-v1.5-7B shape)",
                    "global_batch": b, "seq_len": L, "rank": r, "splits": splits,
-                   "cache_copies": len(copies)},
+                   "cache_copies": n_copies},
         "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
@@ -272,6 +287,7 @@ def main():
         "prefill": prefill,
         "explicit": explicit,
         "headwise": headwise,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
 
@@ -358,6 +374,103 @@ def headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args, rk=64, rv=64):
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                          "algorithmic_bytes": cache_bytes}}
+
+
+def decode_timing(q, torch, step, args):
+    """Step time (HIP events around the timed steps) and per-kernel times (a second pass)."""
+    n = max(args.steps // 2, 5)
+    ms = timed(step, n, args.warmup)
+    with q.timing(max_launches=8 * n + 16) as tm:
+        for i in range(n):
+            step(i)
+    torch.cuda.synchronize()
+    return ms, {k: v[1] / v[0] for k, v in tm.result.items()}
+
+
+def w8a4_leg(q, torch, np, synth, dev, bf, args):
+    """W8A4 decode shape: E = 4096 (32 x 128), r = 768, b = 16, L = 8192.  The cache is the
+    rotated latent C' = C H2^T of the synthetic layer, written as int4 codes with group-128
+    scales by qsvd_quantize_latent (the cache write); W^u' = H2 W^u as int8 columns."""
+    cfg = synth.CONFIGS[2]
+    b, L, r, heads, d = cfg.b, cfg.L, cfg.r, cfg.heads, cfg.d
+    t0 = time.time()
+    cs = synth.decode_case(cfg.E, heads, d, r, b, L, dtype="f32", p=cfg.p, beta=synth.config_beta(cfg),
+                           outlier_frac=cfg.outlier_frac, outlier_gain=cfg.outlier_gain,
+                           hadamard=cfg.hadamard, seed=1000 + cfg.idx)
+    log(f"[bench] generated W8A4 decode inputs ({cfg.name}) in {time.time() - t0:.1f}s")
+    M = b * L
+    Cf = dev(cs.C.reshape(M, r))
+    copies = []
+    for _ in range(max(args.copies, 1)):
+        codes = torch.empty((M, r // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((M, r // 128), dtype=torch.float32, device="cuda")
+        q.qsvd_quantize_latent(Cf, q.F32, M, r, 0, q.I4, 128, codes, scales)
+        copies.append((codes, scales))
+    del Cf
+    Wk_q, Wk_s = synth.int8_columns(np.asarray(cs.Wu_k, np.float64))
+    Wv_q, Wv_s = synth.int8_columns(np.asarray(cs.Wu_v, np.float64))
+    Wk, Wv, wsk, wsv = dev(Wk_q), dev(Wv_q), dev(Wk_s), dev(Wv_s)
+    qv = bf(synth.to_bf16_bits(cs.q))
+    O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(q.qsvd_decode_workspace_bytes(b, L, r, heads, d, q.I4, 0), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        codes, scales = copies[i % len(copies)]
+        q.qsvd_decode_attn(qv, q.BF16, codes, q.I4, scales, 128, Wk, Wv, q.I8, wsk, wsv, b, L, r,
+                           heads, d, cs.softmax_scale, 0, O, q.BF16, ws)
+
+    ms, kern = decode_timing(q, torch, step, args)
+    cache_bytes = b * L * (r // 2 + 4 * (r // 128))
+    stream_ms = kern.get("decode_stream", float("nan"))
+    achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
+    log(f"[bench] W8A4 decode: {ms * 1e3:.1f} us/step; kernels (us): " +
+        ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kern.items()))
+    del copies
+    return {"workload": f"decode step, {cfg.name}: int4 group-128 latent cache (codes + float32 "
+                        "scales), int8 W^u with per-column scales",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(b / (ms * 1e-3), 1),
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+            "roofline": {"bound": "hbm", "kernel": "decode_stream", "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": cache_bytes}}
+
+
+def llava13b_leg(q, torch, synth, bf, args):
+    """13B decode shape: E = 5120 (40 x 128), r = 2304, b = 8, L = 16384, bf16 cache.  The
+    library runs it as two passes (scores, then values), each reading the cache once."""
+    cfg = synth.CONFIGS[3]
+    b, L, r, heads, d = cfg.b, cfg.L, cfg.r, cfg.heads, cfg.d
+    t0 = time.time()
+    cs = synth.config_decode_case(cfg)
+    log(f"[bench] generated 13B decode inputs ({cfg.name}) in {time.time() - t0:.1f}s")
+    C0 = bf(cs.C)
+    cs.C = None
+    copies = [C0] + [C0.clone() for _ in range(max(args.copies, 1) - 1)]
+    qv, Wk, Wv = bf(cs.q), bf(cs.Wu_k), bf(cs.Wu_v)
+    O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(q.qsvd_decode_workspace_bytes(b, L, r, heads, d, q.BF16, 0), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        q.qsvd_decode_attn(qv, q.BF16, copies[i % len(copies)], q.BF16, None, 0, Wk, Wv, q.BF16,
+                           None, None, b, L, r, heads, d, cs.softmax_scale, 0, O, q.BF16, ws)
+
+    ms, kern = decode_timing(q, torch, step, args)
+    cache_bytes = b * L * r * 2
+    stream_ms = kern.get("decode_scores", float("nan")) + kern.get("decode_values", float("nan"))
+    achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
+    moved = 2 * cache_bytes + 2 * b * heads * L * 4    # the cache twice, S written and read
+    log(f"[bench] 13B decode: {ms * 1e3:.1f} us/step; kernels (us): " +
+        ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kern.items()))
+    del copies, C0
+    return {"workload": f"decode step, {cfg.name}: two-pass stream (decode_scores, decode_values)",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(b / (ms * 1e-3), 1),
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+            "pass_bytes_gbps": round(moved / (stream_ms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "kernel": "decode_scores + decode_values",
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": cache_bytes}}
 
 
 def dev_t(torch, np, a):
