@@ -376,6 +376,20 @@ def headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args, rk=64, rv=64):
                          "algorithmic_bytes": cache_bytes}}
 
 
+def counted_traffic(hash_key, source, kernels):
+    """HBM bytes per step of the given kernels from the committed counter passes (FETCH_SIZE and
+    WRITE_SIZE, calibrated), or None when the counters were taken on another source state."""
+    if not os.path.exists(COUNTERS):
+        return None
+    c = json.load(open(COUNTERS))
+    if c.get(hash_key) != source_hash(source):
+        return None
+    other = c.get("other_kernels", {})
+    if not all(k in other for k in kernels):
+        return None
+    return sum(other[k]["hbm_read_bytes"] + other[k]["hbm_write_bytes"] for k in kernels)
+
+
 def decode_timing(q, torch, step, args):
     """Step time (HIP events around the timed steps) and per-kernel times (a second pass)."""
     n = max(args.steps // 2, 5)
@@ -433,7 +447,10 @@ def w8a4_leg(q, torch, np, synth, dev, bf, args):
             "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
             "roofline": {"bound": "hbm", "kernel": "decode_stream", "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": cache_bytes}}
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": counted_traffic("decode_hip_sha256_16", "decode.hip",
+                                                    ["stream_mfma_kernel<1, 2, 4, 64, 1>"]),
+                         "algorithmic_bytes": cache_bytes}}
 
 
 def llava13b_leg(q, torch, synth, bf, args):
@@ -470,7 +487,10 @@ def llava13b_leg(q, torch, synth, bf, args):
             "pass_bytes_gbps": round(moved / (stream_ms * 1e-3) / 1e9, 1),
             "roofline": {"bound": "hbm", "kernel": "decode_scores + decode_values",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": cache_bytes}}
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": counted_traffic("decode_wide_hip_sha256_16", "decode_wide.hip",
+                                                    ["wide_scores_kernel<3, 9>", "wide_values_kernel<3>"]),
+                         "algorithmic_bytes": cache_bytes}}
 
 
 def dev_t(torch, np, a):
