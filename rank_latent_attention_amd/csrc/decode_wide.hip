@@ -295,10 +295,11 @@ void wide_values_kernel(WideArgs p) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[hb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Order of the loads: scores 0, DMA 0, then per tile k the scores of tile
-  // k + 1 and the DMA of tile k + NBUF - 1 (past the end: repeats of the last
-  // tile into a buffer that is not read again), so the count of loads issued
-  // after a tile's DMA is fixed.
+  // Order of the loads: scores 0 (used at once), DMA 0, scores 1 (and DMA 1
+  // with three buffers), then in iteration k the scores of tile k + 2 and the
+  // DMA of tile k + NBUF - 1 (past the end: repeats of the last tile into a
+  // buffer that is not read again), so the count of loads issued after a
+  // tile's DMA is fixed.
   f32x2 snext[NH];
   if (ntiles > 0) {
     f32x2 s0[NH];
