@@ -1,5 +1,6 @@
 """GPU parity for latent caches larger than 4 GiB (64-bit offsets in every
-kernel that walks the cache).
+kernel that walks the cache: the single-pass and two-pass streams, the int4
+stream, the per-head path and the explicit K/V path).
 
 Each case decodes two sequences whose caches are the same periodic sequence
 of rows: row t of the cache is base row t mod P, with P dividing L.  Every
@@ -58,7 +59,6 @@ def _check(O, ref, label):
     (5120, 40, 1792, 1000, 700),
 ], ids=["single_pass", "two_pass"])
 def test_bf16_cache_over_4gib(shape):
-    import torch
     E, heads, r, P, reps = shape
     d, L = 128, P * reps
     assert 2 * L * r * 2 > GIB4
@@ -135,4 +135,28 @@ def test_headwise_cache_over_4gib():
     got = host(outs[True])
     assert np.all(np.isfinite(got)) and np.array_equal(got[0], got[1])
     say("  per-head, RoPE: sequences bitwise equal")
+    _free()
+
+
+def test_explicit_cache_over_4gib():
+    """The explicit K/V path (no rotary positions) over a periodic cache past 4 GiB."""
+    import torch
+    E, heads, d, r, P, reps = 1024, 8, 128, 256, 1000, 4500
+    L = P * reps
+    assert 2 * L * r * 2 > GIB4
+    say(f"case: explicit K/V over 4 GiB E={E} heads={heads} r={r} L={L} (period {P})")
+    cs = synth.decode_case(E, heads, d, r, 1, P, dtype="bf16", hadamard=128, p=0.5, seed=733)
+    C = _periodic(dev(cs.C[0]), reps, 2)
+    qv = dev(np.stack([cs.q[0], cs.q[0]]))
+    Wk_t = dev(np.ascontiguousarray(cs.Wu_k.T))
+    Wv_t = dev(np.ascontiguousarray(cs.Wu_v.T))
+    O = empty((2, heads, d), torch.float32)
+    ws = workspace(q.qsvd_decode_explicit_workspace_bytes(2, L, r, heads, d))
+    q.qsvd_decode_attn_explicit(qv, q.BF16, C, q.BF16, Wk_t, Wv_t, q.BF16, 2, L, r, heads, d,
+                                cs.softmax_scale, None, None, O, q.F32, ws)
+    torch.cuda.synchronize()
+    del C
+    ref = oracle.attend_explicit(values(cs.q, "bf16"), values(cs.C, "bf16"), values(cs.Wu_k, "bf16"),
+                                 values(cs.Wu_v, "bf16"), heads, d, cs.softmax_scale)[0]
+    _check(O, ref, "explicit")
     _free()
