@@ -142,6 +142,17 @@ def test_workspace_and_splits_plan():
     # explicit split counts are honoured up to one token per split
     assert q.qsvd_decode_workspace_bytes(1, 3, 256, 4, 64, q.BF16, 64) == \
         q.qsvd_decode_workspace_bytes(1, 3, 256, 4, 64, q.BF16, 3)
+    # W8A4 shape (int4 cache): one workgroup per CU over 16 sequences
+    assert q.qsvd_decode_default_splits(16, 8192, 768, 32, 128, q.I4) == 16
+    # 13B shape: the two-pass plan holds the score array S[b][heads][L] (float32) and the
+    # value pass's partials, and ignores an explicit split count
+    w13 = q.qsvd_decode_workspace_bytes(8, 16384, 2304, 40, 128, q.BF16)
+    assert w13 >= 8 * 40 * 16384 * 4 + 8 * 10 * 40 * 2304 * 2
+    assert q.qsvd_decode_workspace_bytes(8, 16384, 2304, 40, 128, q.BF16, 3) == w13
+    # per-head latents: the default is 4 splits at the 7B attention shape (512 workgroups)
+    hw = q.qsvd_decode_headwise_workspace_bytes
+    assert hw(16, 8192, 32, 128, 64, 64, 0) == hw(16, 8192, 32, 128, 64, 64, 4) > 0
+    assert hw(16, 8192, 32, 128, 64, 64, 8) > hw(16, 8192, 32, 128, 64, 64, 4)
 
 
 def test_timing_session_errors():
