@@ -75,6 +75,7 @@ BF16_SHAPES = [
     (4096, 32, 128, 1536, 2, 700),
     (5120, 40, 128, 2304, 1, 333),
     (768, 6, 128, 96, 2, 65),
+    (1024, 8, 128, 512, 20, 150),   # more than 16 sequences: a second block of 16 in absorb and merge
 ]
 
 
@@ -190,6 +191,7 @@ WIDE_SHAPES = [
     (64, 2048, 1, 4097),     # four 16-head blocks, one token past a tile
     (33, 2048, 1, 5),        # one valid head in the last block, fewer tokens than a tile
     (48, 2304, 5, 300),      # an odd batch, ragged tiles
+    (40, 2304, 33, 96),      # more than 16 sequences: several sequence blocks in absorb and merge
 ]
 
 
