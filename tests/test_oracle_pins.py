@@ -298,6 +298,31 @@ def test_attention_special_cases():
     assert np.allclose(ob[0].reshape(-1) - oa[0].reshape(-1), c0 @ Wv, rtol=1e-9, atol=1e-9)
 
 
+def test_attention_over_a_repeated_cache():
+    """P11: softmax attention depends on the cached rows only as a multiset with
+    multiplicities; repeating every row k times leaves the output unchanged (the
+    premise of the large-cache GPU tests), for the shared latent and the per-head
+    form, while with rotary positions the repeats sit at new positions and the
+    output changes."""
+    E, heads, d, r, P, k = 256, 4, 64, 96, 7, 3
+    cs = synth.decode_case(E, heads, d, r, 1, P, seed=23)
+    q, C, Wk, Wv = (np.asarray(a, np.float64) for a in (cs.q, cs.C, cs.Wu_k, cs.Wu_v))
+    Crep = np.tile(C, (1, k, 1))                      # row t = base row t mod P
+    base = oracle.attend_explicit(q, C, Wk, Wv, heads, d, 0.125)
+    assert np.allclose(oracle.attend_explicit(q, Crep, Wk, Wv, heads, d, 0.125), base, rtol=1e-12, atol=1e-14)
+    hc = synth.headwise_case(1, P, 2, 128, 32, 32, seed=5)
+    Cb = oracle.bf16_decode(hc.C)
+    BK = np.ascontiguousarray(oracle.bf16_decode(hc.BK_t).transpose(0, 2, 1))
+    BV, qh = oracle.bf16_decode(hc.BV), oracle.bf16_decode(hc.q)
+    Cr = np.tile(Cb, (1, k, 1, 1))
+    hb = oracle.attend_headwise(qh, Cb[..., :32], Cb[..., 32:], BK, BV, hc.softmax_scale, None)
+    hr = oracle.attend_headwise(qh, Cr[..., :32], Cr[..., 32:], BK, BV, hc.softmax_scale, None)
+    assert np.allclose(hr, hb, rtol=1e-12, atol=1e-14)
+    rb = oracle.attend_headwise(qh, Cb[..., :32], Cb[..., 32:], BK, BV, hc.softmax_scale, 50.0)
+    rr = oracle.attend_headwise(qh, Cr[..., :32], Cr[..., 32:], BK, BV, hc.softmax_scale, 50.0)
+    assert not np.allclose(rr, rb, rtol=1e-6, atol=1e-8)
+
+
 def test_attend_heads_subset_matches_full():
     cs = synth.decode_case(256, 4, 64, 96, 2, 40, seed=4)
     full = oracle.attend_explicit(cs.q, cs.C, cs.Wu_k, cs.Wu_v, 4, 64, cs.softmax_scale)
