@@ -1,0 +1,93 @@
+"""The decode entry points inside a captured HIP graph (torch.cuda.graph).
+
+The calls allocate nothing and issue no memset or synchronisation, so a
+runtime can capture a decode step once and replay it.  Each case captures one
+call, then replays it several times with eager work (clearing the output, new
+query values copied into the captured input) and a synchronisation between
+replays, and checks every replay bitwise against an eager call on the same
+inputs.
+"""
+import pytest
+
+import synth
+from gpu_util import dev, empty, say, workspace
+
+import rank_latent_attention_amd as q
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays(call, O, qbuf, qs):
+    """Eager results for each query in qs, then the captured call replayed with each."""
+    import torch
+    eager = []
+    for qv in qs:
+        qbuf.copy_(qv)
+        call()
+        torch.cuda.synchronize()
+        eager.append(O.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        for i, qv in enumerate(qs):
+            O.zero_()
+            qbuf.copy_(qv)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(O, eager[i]), (rep, i)
+    say(f"  {3 * len(qs)} replays bitwise equal to the eager calls")
+
+
+@pytest.mark.parametrize("shape", [
+    # E, heads, r, b, L: single pass; many heads over a wide latent (two passes)
+    (1024, 8, 512, 3, 700),
+    (5120, 40, 2304, 2, 500),
+], ids=["single_pass", "two_pass"])
+def test_decode_attn_graph_replay(shape):
+    import torch
+    E, heads, r, b, L = shape
+    d = 128
+    say(f"case: qsvd_decode_attn in a graph E={E} heads={heads} r={r} b={b} L={L}")
+    cs = synth.decode_case(E, heads, d, r, b, L, dtype="bf16", hadamard=128, seed=61 + r)
+    C, Wk, Wv = dev(cs.C), dev(cs.Wu_k), dev(cs.Wu_v)
+    qbuf = dev(cs.q).clone()
+    qs = [dev(cs.q)]
+    qs.append(torch.flip(qs[0], dims=[1]).contiguous())   # other query values: heads reversed
+    O = empty((b, heads, d), torch.float32)
+    nbytes = q.qsvd_decode_workspace_bytes(b, L, r, heads, d, q.BF16, 0)
+    ws = workspace(nbytes)
+
+    def call():
+        q.qsvd_decode_attn(qbuf, q.BF16, C, q.BF16, None, 0, Wk, Wv, q.BF16, None, None, b, L, r, heads,
+                           d, cs.softmax_scale, 0, O, q.F32, ws)
+
+    _replays(call, O, qbuf, qs)
+
+
+def test_decode_headwise_graph_replay():
+    import torch
+    b, L, heads, d, rk, rv = 2, 600, 8, 128, 64, 64
+    say(f"case: qsvd_decode_attn_headwise in a graph b={b} L={L} heads={heads} RoPE")
+    cs = synth.headwise_case(b, L, heads, d, rk, rv, seed=17)
+    C, BK, BV = dev(cs.C), dev(cs.BK_t), dev(cs.BV)
+    c, s = synth.rope_tables(L, d)
+    rc, rs = dev(c), dev(s)
+    qbuf = dev(cs.q).clone()
+    qs = [dev(cs.q)]
+    qs.append(torch.flip(qs[0], dims=[1]).contiguous())
+    O = empty((b, heads, d), torch.float32)
+    ws = workspace(q.qsvd_decode_headwise_workspace_bytes(b, L, heads, d, rk, rv, 0))
+
+    def call():
+        q.qsvd_decode_attn_headwise(qbuf, q.BF16, C, q.BF16, BK, BV, q.BF16, b, L, heads, d, rk, rv,
+                                    cs.softmax_scale, rc, rs, 0, O, q.F32, ws)
+
+    _replays(call, O, qbuf, qs)
