@@ -1,4 +1,5 @@
-"""The decode entry points inside a captured HIP graph (torch.cuda.graph).
+"""The decode entry points inside a captured HIP graph (torch.cuda.graph), and
+calls on two streams at once.
 
 The calls allocate nothing and issue no memset or synchronisation, so a
 runtime can capture a decode step once and replay it.  Each case captures one
@@ -91,3 +92,46 @@ def test_decode_headwise_graph_replay():
                                     cs.softmax_scale, rc, rs, 0, O, q.F32, ws)
 
     _replays(call, O, qbuf, qs)
+
+
+def test_concurrent_streams_match_sequential():
+    """Two streams (default priority), each with its own inputs, output and workspace, run decode
+    steps concurrently; every result equals the same call run alone (the library keeps no
+    per-call state outside the caller's buffers)."""
+    import torch
+    say("case: concurrent decode calls on two streams")
+    cs = synth.decode_case(1024, 8, 128, 512, 3, 900, dtype="bf16", hadamard=128, seed=71)
+    hc = synth.headwise_case(2, 700, 8, 128, 64, 64, seed=72)
+    C, Wk, Wv, qv = dev(cs.C), dev(cs.Wu_k), dev(cs.Wu_v), dev(cs.q)
+    Ch, BK, BV, qh = dev(hc.C), dev(hc.BK_t), dev(hc.BV), dev(hc.q)
+    O1 = empty((3, 8, 128), torch.float32)
+    O2 = empty((2, 8, 128), torch.float32)
+    ws1 = workspace(q.qsvd_decode_workspace_bytes(3, 900, 512, 8, 128, q.BF16, 0))
+    ws2 = workspace(q.qsvd_decode_headwise_workspace_bytes(2, 700, 8, 128, 64, 64, 0))
+
+    def one():
+        q.qsvd_decode_attn(qv, q.BF16, C, q.BF16, None, 0, Wk, Wv, q.BF16, None, None, 3, 900, 512, 8, 128,
+                           cs.softmax_scale, 0, O1, q.F32, ws1)
+
+    def two():
+        q.qsvd_decode_attn_headwise(qh, q.BF16, Ch, q.BF16, BK, BV, q.BF16, 2, 700, 8, 128, 64, 64,
+                                    hc.softmax_scale, None, None, 0, O2, q.F32, ws2)
+
+    one()
+    two()
+    torch.cuda.synchronize()
+    ref1, ref2 = O1.clone(), O2.clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rnd in range(4):
+        O1.zero_()
+        O2.zero_()
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        for _ in range(3):
+            with torch.cuda.stream(s1):
+                one()
+            with torch.cuda.stream(s2):
+                two()
+        torch.cuda.synchronize()
+        assert torch.equal(O1, ref1) and torch.equal(O2, ref2), rnd
+    say("  4 rounds of interleaved launches equal the sequential results")
