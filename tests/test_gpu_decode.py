@@ -210,6 +210,22 @@ def test_two_pass_decode(shape):
     assert np.array_equal(decode_case_on_gpu(cs, splits=5), got)
 
 
+def test_two_pass_with_int8_up_projections():
+    """Two-pass decode of a bf16 cache with W^u stored as int8 columns (absorb and merge dequantise)."""
+    heads, r, b, L, d = 40, 2304, 2, 700, 128
+    say(f"case: two-pass decode, int8 W^u, heads={heads} r={r} b={b} L={L}")
+    cs = synth.decode_case(heads * d, heads, d, r, b, L, dtype="bf16", hadamard=128, seed=93)
+    Wk_q, Wk_s = synth.int8_columns(values(cs.Wu_k, "bf16"))
+    Wv_q, Wv_s = synth.int8_columns(values(cs.Wu_v, "bf16"))
+    O = decode(dev(cs.q), q.BF16, dev(cs.C), q.BF16, dev(Wk_q), dev(Wv_q), q.I8, b, L, r, heads, d,
+               cs.softmax_scale, wsk=dev(Wk_s), wsv=dev(Wv_s))
+    ref = oracle.attend_explicit(values(cs.q, "bf16"), values(cs.C, "bf16"), oracle.dequant_cols(Wk_q, Wk_s),
+                                 oracle.dequant_cols(Wv_q, Wv_s), heads, d, cs.softmax_scale)
+    err = oracle.rel_l2(host(O), ref)
+    say(f"  rel-L2 {err:.2e}")
+    assert err <= TOL_BF16
+
+
 @pytest.mark.parametrize("heads,r,L", [(40, 2304, 1500), (64, 2048, 1300)], ids=["h40", "h64"])
 @pytest.mark.parametrize("factor", [30.0, 300.0])
 def test_two_pass_sharpened_softmax(factor, heads, r, L):
