@@ -57,8 +57,6 @@ enum CType : int { CT_BF16 = 0, CT_I4 = 1, CT_I8 = 2 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
-
 // ------------------------------------------------------------------ absorb
 // q~[b][h][j] = scale * sum_i Wk[j][h d + i] * q[b][h][i].  One workgroup owns
 // 16 rows j of one head; 16 lanes split the d-wide row segment.

@@ -89,7 +89,6 @@ void explicit_attn_kernel(const uint16_t *__restrict__ q, const uint8_t *__restr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int64_t kbytes = static_cast<int64_t>(r) * 2;
-  const int64_t E = static_cast<int64_t>(heads) * kD;
 
   float *qr = reinterpret_cast<float *>(lds + kQrOff);
   float *ps = reinterpret_cast<float *>(lds + kPsOff);
