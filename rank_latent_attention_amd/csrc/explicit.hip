@@ -44,6 +44,7 @@ using dma::wait_all_loads;
 constexpr float kLog2eX = 1.4426950408889634f;
 constexpr int kD = 128;                    // head dimension of this variant
 constexpr int kTok = 256;                  // tokens per workgroup
+constexpr int kTG = 8;                     // tiles per group of the XCD-aware order
 constexpr int kBN = 2 * kD;                // [K_h | V_h] columns
 constexpr int kSlot = (kTok + kBN) * BK;   // one LDS stage (64 KB)
 constexpr int kKtStride = kTok + 4;        // K^T row stride (floats)
@@ -74,15 +75,29 @@ void explicit_attn_kernel(const uint16_t *__restrict__ q, const uint8_t *__restr
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int64_t ntiles = (L + kTok - 1) / kTok;
-  int64_t task;
-  {
+  int h;
+  int64_t tile, seq;
+  if (heads % 8 == 0) {
+    // XCD x (workgroup id mod 8) owns heads x * heads / 8 ..; its concurrent
+    // workgroups cover those heads for one group of kTG tiles, which all XCDs
+    // work on at the same time: each XCD's L2 keeps its heads' W^u rows, and
+    // the group's latent rows come from HBM about once for all eight XCDs.
+    const int hpx = heads / 8;
+    const int64_t id = blockIdx.x, local = id / 8;
+    const int64_t ngroups = (ntiles + kTG - 1) / kTG;
+    const int64_t rest = local / hpx, rest2 = rest / kTG;
+    h = static_cast<int>(id % 8) * hpx + static_cast<int>(local % hpx);
+    tile = (rest2 % ngroups) * kTG + rest % kTG;
+    seq = rest2 / ngroups;
+    if (tile >= ntiles) return;   // padding of the last tile group (the whole workgroup)
+  } else {
     const int total = gridDim.x, id = blockIdx.x;
     const int per = total / 8, rem = total % 8, xcd = id % 8, local = id / 8;
-    task = xcd * per + min(xcd, rem) + local;   // the heads of one tile share an XCD's L2
+    const int64_t task = xcd * per + min(xcd, rem) + local;   // the heads of one tile share an XCD's L2
+    h = static_cast<int>(task % heads);
+    tile = (task / heads) % ntiles;
+    seq = task / (static_cast<int64_t>(heads) * ntiles);
   }
-  const int h = static_cast<int>(task % heads);
-  const int64_t tile = (task / heads) % ntiles;
-  const int64_t seq = task / (static_cast<int64_t>(heads) * ntiles);
   const int64_t t0 = tile * kTok;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -330,7 +345,9 @@ size_t explicit_workspace_bytes(int b, int64_t L, int heads) {
 
 hipError_t launch_decode_explicit(const ExplicitArgs &a, hipStream_t s) {
   const int64_t ntiles = (a.L + kTok - 1) / kTok;
-  const int64_t total = static_cast<int64_t>(a.b) * ntiles * a.heads;
+  const int64_t total = a.heads % 8 == 0
+                            ? static_cast<int64_t>(a.b) * a.heads * ((ntiles + kTG - 1) / kTG) * kTG
+                            : static_cast<int64_t>(a.b) * ntiles * a.heads;
   float *part = static_cast<float *>(a.workspace);
   const float scale_log2 = a.softmax_scale * kLog2eX;
   {

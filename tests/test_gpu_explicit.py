@@ -52,6 +52,7 @@ SHAPES = [
     (1024, 8, 512, 1, 513),     # one token past two tiles
     (2048, 16, 1536, 1, 77),    # r of the 7B shape, one partial tile
     (512, 4, 128, 3, 1),        # a single cached latent
+    (1024, 8, 256, 3, 2500),    # two groups of eight tiles per sequence, the last one partial
 ]
 
 
