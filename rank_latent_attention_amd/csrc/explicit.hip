@@ -203,6 +203,19 @@ void explicit_attn_kernel(const uint16_t *__restrict__ q, const uint8_t *__restr
 
   // ---- 1. K^T to LDS.  Accumulator element e of lane l: row 8 (e / 4) +
   // 4 (l / 32) + e % 4 of the 32-row block, column l % 32.
+  // (The rotary rows of this thread's token are requested first, so they
+  // arrive while the keys go to LDS.)
+  f32x4 rcs[ROPE ? 8 : 1], rsn[ROPE ? 8 : 1];
+  if constexpr (ROPE) {
+    const int64_t pos = t0 + (tid & (kTok - 1));
+    const int64_t prow = (pos < L ? pos : L - 1) * (kD / 2);
+#pragma unroll
+    for (int i4 = 0; i4 < 8; ++i4) {
+      const int i0 = (tid >> 8) * 32 + 4 * i4;
+      rcs[i4] = *reinterpret_cast<const f32x4 *>(rope_cos + prow + i0);
+      rsn[i4] = *reinterpret_cast<const f32x4 *>(rope_sin + prow + i0);
+    }
+  }
   float *kt = reinterpret_cast<float *>(lds);
   if (wn < 2) {
 #pragma unroll
@@ -225,12 +238,11 @@ void explicit_attn_kernel(const uint16_t *__restrict__ q, const uint8_t *__restr
     const int64_t pos = t0 + t;
     float s = 0.f;
     if constexpr (ROPE) {
-      const int64_t prow = (pos < L ? pos : L - 1) * (kD / 2);
 #pragma unroll
       for (int i4 = 0; i4 < 8; ++i4) {
         const int i0 = half * 32 + 4 * i4;
-        const f32x4 cs = *reinterpret_cast<const f32x4 *>(rope_cos + prow + i0);
-        const f32x4 sn = *reinterpret_cast<const f32x4 *>(rope_sin + prow + i0);
+        const f32x4 cs = rcs[i4];
+        const f32x4 sn = rsn[i4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = i0 + u;
