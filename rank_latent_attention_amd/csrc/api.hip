@@ -232,6 +232,11 @@ static qsvd_status_t validate_explicit_shape(int32_t b, int64_t L, int32_t r, in
     return fail(QSVD_ERR_INVALID, "decode_explicit: r = %d (a multiple of 64, 64..16384)", r);
   if (static_cast<int64_t>(b) * L > (int64_t(1) << 36))
     return fail(QSVD_ERR_INVALID, "decode_explicit: b * L too large");
+  // one workgroup per (sequence, 256-token tile, head), tiles padded to groups
+  // of 8 (a 1-D launch)
+  const int64_t groups = ((L + 255) / 256 + 7) / 8;
+  if (static_cast<int64_t>(b) * heads * groups * 8 > 0x7FFFFFFF)
+    return fail(QSVD_ERR_INVALID, "decode_explicit: b * heads * L / 256 too large for one launch");
   return QSVD_OK;
 }
 

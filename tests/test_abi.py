@@ -183,6 +183,8 @@ def test_decode_explicit_validation():
     assert st_exp(odt=q.I8) == -1
     assert st_exp(rc=FAKE) == -1                  # the two tables go together
     assert st_exp(scale=-1.0) == -1
+    # more workgroups than one launch holds: rejected before any launch
+    assert st_exp(b=1024, L=1 << 26, heads=256) == -1
     assert st_exp(Wv=None) == -1
     assert st_exp(rc=ctypes.c_void_p((1 << 20) + 4), rs=FAKE) == -1
     need = q.qsvd_decode_explicit_workspace_bytes(2, 300, 256, 4, 128)
