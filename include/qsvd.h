@@ -160,7 +160,7 @@ qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int
  *     F32  : q, C, W^u, O all F32 (float32 arithmetic throughout).
  *     BF16 : q, C, W^u BF16; O BF16 or F32 (bf16 MFMA, float32 accumulation).
  *     I4/I8: q BF16, W^u BF16 or I8; O BF16 or F32.
- *   Constraints: E == heads * d, d % 16 == 0, heads <= 256, L >= 1, b >= 1;
+ *   Constraints: E == heads * d, d % 16 == 0, heads <= 256, L >= 1, 1 <= b <= 65535;
  *   F32: 1 <= r <= 4096;  other caches: r % 32 == 0 and r / W <= 288, where W
  *   is the largest of 8, 4, 2, 1 with r % (32 W) == 0 (so r <= 2304 for
  *   r % 256 == 0);  I4: r % 128 == 0.  d is 16, 32, 64, 128 or 256.

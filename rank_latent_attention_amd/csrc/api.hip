@@ -186,7 +186,8 @@ qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int
 
 static qsvd_status_t validate_decode_shape(int32_t b, int64_t L, int32_t r, int32_t heads,
                                            int32_t d, qsvd_dtype_t c_dtype, int32_t splits) {
-  if (b < 1) return fail(QSVD_ERR_INVALID, "decode: b = %d < 1", b);
+  // b <= 65535: the absorb, merge and float32 stream launches put the batch in a grid dimension
+  if (b < 1 || b > 65535) return fail(QSVD_ERR_INVALID, "decode: b = %d (1..65535)", b);
   if (L < 1) return fail(QSVD_ERR_INVALID, "decode: L = %lld < 1", (long long)L);
   if (heads < 1 || heads > 256) return fail(QSVD_ERR_INVALID, "decode: heads = %d (1..256)", heads);
   if (d != 16 && d != 32 && d != 64 && d != 128 && d != 256)

@@ -102,6 +102,7 @@ def st_dec(**kw):
 
 def test_decode_validation():
     assert st_dec(b=0) == -1
+    assert st_dec(b=65536) == -1                  # the batch fills a grid dimension
     assert st_dec(L=0) == -1
     assert st_dec(d=48) == -2
     assert st_dec(r=100) == -1                    # bf16 cache needs r % 32
