@@ -172,7 +172,11 @@ def unpack_int4(packed) -> np.ndarray:
 
 
 def dequant_rows(codes, scales, group: int = 0) -> np.ndarray:
-    """code x scale per token (group == 0) or per token group; exact in float64."""
+    """code x scale per token (group == 0) or per token and `group`-wide column
+    group (the W8A4 latent of [QSVD-notes] "Main results"); exact in float64.
+    Pinned by hand-built rows (each group's scale touches only its own columns
+    and row), the |dequant(quantise(y)) - y| <= s/2 bound through int4 packing,
+    and an element loop on batched [b][L][r] codes."""
     c = np.asarray(codes, dtype=np.float64)
     s = np.asarray(scales, dtype=np.float64)
     if group == 0:
@@ -182,7 +186,9 @@ def dequant_rows(codes, scales, group: int = 0) -> np.ndarray:
 
 
 def dequant_cols(codes, col_scale) -> np.ndarray:
-    """Per-output-column int8 weights: W[k][n] = code[k][n] x scale[n]."""
+    """Per-output-column int8 weights: W[k][n] = code[k][n] x scale[n] (the W8
+    weights of [QSVD-notes] "Main results").  Pinned by a hand-built non-square
+    case whose values change if the scale runs along rows."""
     return np.asarray(codes, np.float64) * np.asarray(col_scale, np.float64)[None, :]
 
 
@@ -228,7 +234,8 @@ def project_int32(x_codes, w_codes) -> np.ndarray:
 
 
 def project_real(x, w) -> np.ndarray:
-    """Real-valued product for the bf16 / float32 projection (compared with a tolerance)."""
+    """Real-valued product for the bf16 / float32 projection (compared with a
+    tolerance).  Pinned by a brute-force triple loop."""
     return np.asarray(x, np.float64) @ np.asarray(w, np.float64)
 
 

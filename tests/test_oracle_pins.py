@@ -254,6 +254,84 @@ def test_quantiser_groups_are_independent():
     assert scales[0, 0] == np.float32(1.0) and scales[0, 1] == np.float32(0.5) / np.float32(7.0)
 
 
+# ------------------------------------------------------------- dequantisers
+def test_dequant_rows_hand_built_groups():
+    """Per-token-group scales touch only their own 128 columns and their own row
+    (QSVD notes, 'Main results': W8A4 caches int4 latents with group scales).
+    A scale broadcast along the wrong axis, or groups taken in the wrong order,
+    changes a hand-derived value below."""
+    codes = np.ones((2, 256), dtype=np.int8)
+    codes[1, :] = -3
+    codes[0, 130] = 5
+    scales = np.array([[2.0, 0.5], [0.25, 8.0]], dtype=np.float32)
+    got = oracle.dequant_rows(codes, scales, 128)
+    assert got.shape == (2, 256)
+    assert np.all(got[0, :128] == 2.0) and got[0, 129] == 0.5 and got[0, 130] == 2.5
+    assert np.all(got[1, :128] == -0.75) and np.all(got[1, 128:] == -24.0)
+    # per-token scales (group 0): row i scales by scales[i] only; 3 x 5 is not
+    # square, so a transposed broadcast fails on shape or value
+    c0 = np.arange(15, dtype=np.int8).reshape(3, 5) - 7
+    s0 = np.array([1.0, 10.0, 100.0], dtype=np.float32)
+    got0 = oracle.dequant_rows(c0, s0, 0)
+    for i in range(3):
+        for j in range(5):
+            assert got0[i, j] == float(c0[i, j]) * float(s0[i])
+    # batched leading axes, as the [b][L][r] caches use them
+    c3 = np.random.default_rng(5).integers(-7, 8, size=(2, 3, 256)).astype(np.int8)
+    s3 = np.random.default_rng(6).random((2, 3, 2)).astype(np.float32)
+    got3 = oracle.dequant_rows(c3, s3, 128)
+    for b in range(2):
+        for t in range(3):
+            for j in range(256):
+                assert got3[b, t, j] == float(c3[b, t, j]) * float(s3[b, t, j // 128])
+
+
+@pytest.mark.parametrize("bits,group", [(8, 0), (4, 0), (4, 128)])
+def test_dequant_reconstructs_within_half_a_step(bits, group):
+    """|dequant(quantise(y)) - y| <= s/2 in every group, through the int4
+    packing where the cache uses it; checked with an element loop that does
+    not call the dequantiser's broadcasting."""
+    g = np.random.default_rng(40 + bits + group)
+    y = oracle.fl32(g.standard_normal((4, 384)) * np.array([1.0, 30.0, 1e-3, 7.0])[:, None])
+    y[2, 200:300] *= 1e4                      # one loud group next to quiet ones
+    codes, scales = oracle.quantize_rows(y, bits, group)
+    if bits == 4:
+        codes = oracle.unpack_int4(oracle.pack_int4(codes))
+    rec = oracle.dequant_rows(codes, scales, group)
+    gs = 384 if group == 0 else group
+    for i in range(4):
+        for j in range(384):
+            s = float(scales[i]) if group == 0 else float(scales[i, j // gs])
+            assert rec[i, j] == float(codes[i, j]) * s
+            assert abs(rec[i, j] - y[i, j]) <= 0.5 * s * (1 + 1e-6)
+    # the quiet groups of row 2 keep their own (small) step
+    if group == 128:
+        assert scales[2, 0] < scales[2, 1] / 100
+
+
+def test_dequant_cols_scales_columns_not_rows():
+    """Per-output-column int8 weights (W8): W[k][n] = code[k][n] x scale[n]."""
+    codes = np.array([[1, -2], [3, 4], [-5, 6]], dtype=np.int8)     # [K=3][N=2]
+    scale = np.array([10.0, 0.5], dtype=np.float32)
+    got = oracle.dequant_cols(codes, scale)
+    assert got.tolist() == [[10.0, -1.0], [30.0, 2.0], [-50.0, 3.0]]
+
+
+def test_project_real_brute_force():
+    """The real-valued projection equals a triple-loop sum over k."""
+    g = np.random.default_rng(8)
+    x = g.standard_normal((3, 7))
+    w = g.standard_normal((7, 5))
+    got = oracle.project_real(x, w)
+    assert got.shape == (3, 5)
+    for m in range(3):
+        for n in range(5):
+            acc = 0.0
+            for k in range(7):
+                acc += x[m, k] * w[k, n]
+            assert abs(got[m, n] - acc) <= 1e-14 * (1 + sum(abs(x[m, k] * w[k, n]) for k in range(7)))
+
+
 # ------------------------------------------------------------- P10 GEMM
 def test_int8_projection_exact_and_epilogue():
     """P10: int32 accumulators equal a brute-force integer product; the epilogue
