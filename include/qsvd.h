@@ -45,14 +45,24 @@
 extern "C" {
 #endif
 
-typedef enum qsvd_dtype {
+/* In C++ the enums below get int32_t as their fixed underlying type, so an
+ * out-of-range value passed across the C ABI is a valid (and rejected)
+ * argument rather than undefined behaviour; the size and passing convention
+ * are those of the C enums (int). */
+#ifdef __cplusplus
+#define QSVD_ENUM_BASE : int32_t
+#else
+#define QSVD_ENUM_BASE
+#endif
+
+typedef enum qsvd_dtype QSVD_ENUM_BASE {
   QSVD_F32 = 0,   /* IEEE binary32 */
   QSVD_BF16 = 1,  /* bfloat16 */
   QSVD_I8 = 2,    /* int8 codes (symmetric, +-127) */
   QSVD_I4 = 3     /* packed int4 codes (symmetric, +-7) */
 } qsvd_dtype_t;
 
-typedef enum qsvd_status {
+typedef enum qsvd_status QSVD_ENUM_BASE {
   QSVD_OK = 0,
   QSVD_ERR_INVALID = -1,      /* bad shape, pointer, alignment or argument */
   QSVD_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
@@ -160,10 +170,10 @@ qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int
  *     F32  : q, C, W^u, O all F32 (float32 arithmetic throughout).
  *     BF16 : q, C, W^u BF16; O BF16 or F32 (bf16 MFMA, float32 accumulation).
  *     I4/I8: q BF16, W^u BF16 or I8; O BF16 or F32.
- *   Constraints: E == heads * d, d % 16 == 0, heads <= 256, L >= 1, 1 <= b <= 65535;
+ *   Constraints: E == heads * d, heads <= 256, L >= 1, 1 <= b <= 65535;
  *   F32: 1 <= r <= 4096;  other caches: r % 32 == 0 and r / W <= 288, where W
  *   is the largest of 8, 4, 2, 1 with r % (32 W) == 0 (so r <= 2304 for
- *   r % 256 == 0);  I4: r % 128 == 0.  d is 16, 32, 64, 128 or 256.
+ *   r % 256 == 0);  I4: r % 128 == 0.  d is 64 or 128 (QSVD_ERR_UNSUPPORTED otherwise).
  */
 size_t qsvd_decode_workspace_bytes(int32_t b, int64_t L, int32_t r, int32_t heads, int32_t d,
                                    qsvd_dtype_t c_dtype, int32_t splits);

@@ -79,6 +79,29 @@ LaunchTimer::~LaunchTimer() {
   (void)hipEventRecord(g_timing.records[slot_].stop, stream_);
 }
 
+hipError_t set_dynamic_lds(const void *kernel, size_t bytes) {
+  struct Entry {
+    const void *fn;
+    int device;
+    size_t bytes;
+  };
+  thread_local std::vector<Entry> done;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return e;
+  Entry *hit = nullptr;
+  for (Entry &x : done)
+    if (x.fn == kernel && x.device == device) hit = &x;
+  if (hit && hit->bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e != hipSuccess) return e;
+  if (hit)
+    hit->bytes = bytes;
+  else
+    done.push_back(Entry{kernel, device, bytes});
+  return hipSuccess;
+}
+
 }  // namespace qsvd
 
 extern "C" {
@@ -190,8 +213,7 @@ static qsvd_status_t validate_decode_shape(int32_t b, int64_t L, int32_t r, int3
   if (b < 1 || b > 65535) return fail(QSVD_ERR_INVALID, "decode: b = %d (1..65535)", b);
   if (L < 1) return fail(QSVD_ERR_INVALID, "decode: L = %lld < 1", (long long)L);
   if (heads < 1 || heads > 256) return fail(QSVD_ERR_INVALID, "decode: heads = %d (1..256)", heads);
-  if (d != 16 && d != 32 && d != 64 && d != 128 && d != 256)
-    return fail(QSVD_ERR_UNSUPPORTED, "decode: d = %d (16, 32, 64, 128 or 256)", d);
+  if (d != 64 && d != 128) return fail(QSVD_ERR_UNSUPPORTED, "decode: d = %d (64 or 128)", d);
   if (splits < 0) return fail(QSVD_ERR_INVALID, "decode: splits = %d < 0", splits);
   if (c_dtype == QSVD_F32) {
     if (r < 1 || r > 4096) return fail(QSVD_ERR_UNSUPPORTED, "decode: F32 cache needs 1 <= r <= 4096");
@@ -206,7 +228,7 @@ static qsvd_status_t validate_decode_shape(int32_t b, int64_t L, int32_t r, int3
   } else {
     return fail(QSVD_ERR_INVALID, "decode: c_dtype %s", dtype_name(c_dtype));
   }
-  if (static_cast<int64_t>(b) * L > (int64_t(1) << 40))
+  if (L > (int64_t(1) << 40) / b)   // b * L <= 2^40, without overflow
     return fail(QSVD_ERR_INVALID, "decode: b * L too large");
   return QSVD_OK;
 }
@@ -231,7 +253,7 @@ static qsvd_status_t validate_explicit_shape(int32_t b, int64_t L, int32_t r, in
   if (d != 128) return fail(QSVD_ERR_UNSUPPORTED, "decode_explicit: d = %d (128)", d);
   if (r < 64 || r % 64 != 0 || r > 16384)
     return fail(QSVD_ERR_INVALID, "decode_explicit: r = %d (a multiple of 64, 64..16384)", r);
-  if (static_cast<int64_t>(b) * L > (int64_t(1) << 36))
+  if (L > (int64_t(1) << 36) / b)   // b * L <= 2^36, without overflow
     return fail(QSVD_ERR_INVALID, "decode_explicit: b * L too large");
   // one workgroup per (sequence, 256-token tile, head), tiles padded to groups
   // of 8 (a 1-D launch)
@@ -306,7 +328,7 @@ static qsvd_status_t validate_headwise_shape(int32_t b, int64_t L, int32_t heads
                 rk, rv);
   if (splits < 0 || splits > 1024)
     return fail(QSVD_ERR_INVALID, "decode_headwise: splits = %d (0..1024)", splits);
-  if (static_cast<int64_t>(b) * L > (int64_t(1) << 36))
+  if (L > (int64_t(1) << 36) / b)   // b * L <= 2^36, without overflow
     return fail(QSVD_ERR_INVALID, "decode_headwise: b * L too large");
   const int64_t grid = static_cast<int64_t>(b) * qsvd::headwise_splits(b, L, heads, splits) *
                        ((heads + 3) / 4);

@@ -1050,9 +1050,7 @@ template <int CT, int NHB, int NKB, int T, int D>
 hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
   auto kern = stream_mfma_kernel<CT, NHB, NKB, T, D>;
   const size_t lds = stream_lds_bytes(W, NHB, NKB, T);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(sp.ntasks), dim3(W * 64), lds, s>>>(sp);
   return hipGetLastError();
@@ -1126,9 +1124,7 @@ template <int MJ>
 hipError_t run_stream_f32(dim3 grid, size_t lds, hipStream_t s, const float *C, const float *q,
                           float *op, float *ml, const DecodeArgs &a, const DecodePlan &p) {
   auto kern = stream_f32_kernel<MJ>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<grid, dim3(256), lds, s>>>(C, q, op, ml, a.L, a.r, a.heads, p.splits, p.chunk);
   return hipGetLastError();
@@ -1140,14 +1136,9 @@ hipError_t launch_absorb_t(const DecodeArgs &a, OT *qt, hipStream_t s) {
   const float scale = a.softmax_scale * kLog2e;
   const auto *q = static_cast<const QT *>(a.q);
   const auto *w = static_cast<const WT *>(a.Wu_k);
-  const int epp = a.d / 16;
-  switch (epp) {
-    case 1: return run_absorb<QT, WT, OT, 1>(grid, s, q, w, a, qt, scale);
-    case 2: return run_absorb<QT, WT, OT, 2>(grid, s, q, w, a, qt, scale);
-    case 4: return run_absorb<QT, WT, OT, 4>(grid, s, q, w, a, qt, scale);
-    case 8: return run_absorb<QT, WT, OT, 8>(grid, s, q, w, a, qt, scale);
-    default: return run_absorb<QT, WT, OT, 16>(grid, s, q, w, a, qt, scale);
-  }
+  // d is 64 or 128 (validated by the caller): 16 lanes take d / 16 elements each
+  if (a.d == 64) return run_absorb<QT, WT, OT, 4>(grid, s, q, w, a, qt, scale);
+  return run_absorb<QT, WT, OT, 8>(grid, s, q, w, a, qt, scale);
 }
 
 hipError_t launch_merge_f32(const DecodeArgs &a, const DecodePlan &p, const float *opart,
@@ -1155,9 +1146,7 @@ hipError_t launch_merge_f32(const DecodeArgs &a, const DecodePlan &p, const floa
   const int JC = (a.r + kMergeRows - 1) / kMergeRows;
   const size_t lds = (static_cast<size_t>(16) * p.splits + 16 * kMergeRows) * sizeof(float);
   auto kern = merge_f32_kernel<float, float>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
       opart, ml, static_cast<const float *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
@@ -1176,9 +1165,7 @@ hipError_t launch_merge_mfma(const DecodeArgs &a, const DecodePlan &p, const uin
   const int JC = (a.r + kMergeRows - 1) / kMergeRows;
   const size_t lds = merge_mfma_lds(a.d, p.splits);
   auto kern = merge_mfma_kernel<WT>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
       opart, ml, static_cast<const WT *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
@@ -1197,12 +1184,9 @@ hipError_t launch_absorb_mfma_t(const DecodeArgs &a, uint16_t *qt, hipStream_t s
 
 template <typename WT>
 hipError_t launch_absorb_mfma(const DecodeArgs &a, uint16_t *qt, hipStream_t s) {
-  switch (a.d) {
-    case 32: return launch_absorb_mfma_t<WT, 1>(a, qt, s);
-    case 64: return launch_absorb_mfma_t<WT, 2>(a, qt, s);
-    case 128: return launch_absorb_mfma_t<WT, 4>(a, qt, s);
-    default: return launch_absorb_mfma_t<WT, 8>(a, qt, s);
-  }
+  // d is 64 or 128 (validated by the caller)
+  if (a.d == 64) return launch_absorb_mfma_t<WT, 2>(a, qt, s);
+  return launch_absorb_mfma_t<WT, 4>(a, qt, s);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1319,15 +1303,10 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
     LaunchTimer t("decode_absorb", s);
     if (!p.mfma) {
       e = launch_absorb_t<float, float, float>(a, static_cast<float *>(qt), s);
-    } else if (a.d % 32 == 0) {
-      if (a.wu_dtype == QSVD_I8)
-        e = launch_absorb_mfma<int8_t>(a, static_cast<uint16_t *>(qt), s);
-      else
-        e = launch_absorb_mfma<uint16_t>(a, static_cast<uint16_t *>(qt), s);
     } else if (a.wu_dtype == QSVD_I8) {
-      e = launch_absorb_t<uint16_t, int8_t, uint16_t>(a, static_cast<uint16_t *>(qt), s);
+      e = launch_absorb_mfma<int8_t>(a, static_cast<uint16_t *>(qt), s);
     } else {
-      e = launch_absorb_t<uint16_t, uint16_t, uint16_t>(a, static_cast<uint16_t *>(qt), s);
+      e = launch_absorb_mfma<uint16_t>(a, static_cast<uint16_t *>(qt), s);
     }
     if (e != hipSuccess) return e;
   }

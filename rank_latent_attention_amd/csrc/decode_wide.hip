@@ -179,7 +179,7 @@ __global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
 // Workgroup (sequence, split, 256-column chunk cc), 4 wavefronts of 64
 // columns each.  The split's maximum per head comes from the score pass's
 // chunk maxima.  A 32-token tile (32 rows x 512 bytes) moves from memory
-// straight into an LDS buffer by buffer_load ... lds, NBUF - 1 tiles ahead of
+// straight into an LDS buffer by buffer_load ... lds, one tile ahead of
 // the one in use; in LDS the 16-byte chunk c of row R sits at c ^ vsw(R), so
 // the 4 rows of a transposing read fall in distinct banks.  The probabilities
 // p = 2^(S - m) of a tile are formed once per workgroup, one tile ahead
@@ -191,8 +191,13 @@ __device__ __forceinline__ int vsw(int row) { return 2 * (row & 3); }
 
 // workgroups of the value pass per compute unit (its register budget)
 constexpr int wide_values_per_cu(int nh) { return nh <= 3 ? 3 : 2; }
-// LDS tile buffers: as many as that many workgroups hold beside the p fragments
-constexpr int wide_values_bufs(int nh) { return nh <= 3 ? 2 : 3; }
+// LDS tile buffers: the tile in use and the one in flight.  The loop waits for
+// every outstanding vector-memory operation (vmcnt 0) before it reads a tile
+// that arrived by LDS DMA: the compiler does not track those loads, and a
+// wait that counted the instructions issued after the DMA would silently
+// release early if code generation split or merged one of them.  A third
+// buffer would add nothing under that wait.
+constexpr int wide_values_bufs(int) { return 2; }
 
 template <int NH>
 __global__ __launch_bounds__(256)
@@ -203,10 +208,10 @@ void wide_values_kernel(WideArgs p) {
   constexpr int NJB = kWideCW / kWideVW / 16;   // 16-column blocks per wavefront
   constexpr int NBUF = wide_values_bufs(NH);
   constexpr int PB = NH * 64 * 16;              // bytes of a tile's p fragments
-  // vmcnt once a tile's DMA has landed: the loads issued after it are the
-  // next tiles' score loads (NH) and DMA (4), NBUF - 2 groups of them
-  constexpr int kAfter = (NBUF - 2) * (NH + 4);
-  constexpr int kWaitImm = (kAfter & 15) | ((kAfter >> 4) << 14) | 0x0070 | 0x0F00;
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): every load
+  // issued so far, the DMA of the tile about to be read included, has landed
+  constexpr int kWaitImm = 0x0070 | 0x0F00;
+  static_assert(NBUF == 2, "the full vmcnt wait leaves nothing for a third buffer to overlap");
   __shared__ __attribute__((aligned(1024))) uint8_t ct[NBUF][TB];
   __shared__ __attribute__((aligned(16))) uint8_t pf[2][PB];
   __shared__ float lred[kWideVW][NH * 16];
@@ -295,11 +300,9 @@ void wide_values_kernel(WideArgs p) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[hb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Order of the loads: scores 0 (used at once), DMA 0, scores 1 (and DMA 1
-  // with three buffers), then in iteration k the scores of tile k + 2 and the
-  // DMA of tile k + NBUF - 1 (past the end: repeats of the last tile into a
-  // buffer that is not read again), so the count of loads issued after a
-  // tile's DMA is fixed.
+  // Order of the loads: scores 0 (used at once), DMA 0, scores 1, then in
+  // iteration k the scores of tile k + 2 and the DMA of tile k + 1 (past the
+  // end: repeats of the last tile into a buffer that is not read again).
   f32x2 snext[NH];
   if (ntiles > 0) {
     f32x2 s0[NH];
@@ -309,7 +312,6 @@ void wide_values_kernel(WideArgs p) {
     dma_tile(0, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_scores(min(1, ntiles - 1), snext);
-    if constexpr (NBUF == 3) dma_tile(min(1, ntiles - 1), 1);
     __builtin_amdgcn_sched_barrier(0);
   }
   for (int it = 0; it < ntiles; ++it) {
@@ -388,8 +390,7 @@ template <int NH, int NKB>
 hipError_t launch_scores_t(const WideArgs &a, hipStream_t s) {
   auto kern = wide_scores_kernel<NH, NKB>;
   const size_t lds = static_cast<size_t>(kWideW) * NH * 16 * (kWideT + 4) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(static_cast<unsigned>(a.b * a.nchunk1)), dim3(64 * kWideW), lds, s>>>(a);
   return hipGetLastError();

@@ -365,8 +365,7 @@ hipError_t launch_decode_explicit(const ExplicitArgs &a, hipStream_t s) {
   {
     LaunchTimer t("explicit_attn", s);
     auto kern = a.rope_cos ? explicit_attn_kernel<true> : explicit_attn_kernel<false>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), kLdsBytes);
     if (e != hipSuccess) return e;
     kern<<<dim3(static_cast<unsigned>(total)), dim3(512), kLdsBytes, s>>>(
         static_cast<const uint16_t *>(a.q), static_cast<const uint8_t *>(a.C),

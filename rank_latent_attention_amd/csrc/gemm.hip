@@ -301,8 +301,7 @@ hipError_t run_gemm(const uint8_t *a, const float *a_scale, int64_t M, int K, co
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   constexpr size_t lds = static_cast<size_t>(2) * (BM + BN) * BK;
   auto kern = gemm_kernel<INT8, OUT_BF16, BM, BN, WM, WN, INT4>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(static_cast<unsigned>(tiles)), dim3(64 * WM * WN), lds, s>>>(a, a_scale, M, K, b,
                                                                           col_scale, N, C);

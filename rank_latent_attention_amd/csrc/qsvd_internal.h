@@ -25,6 +25,12 @@ class LaunchTimer {
   hipStream_t stream_;
 };
 
+// Allow `kernel` (a __global__ function's address) `bytes` of dynamic LDS on
+// the current device.  The attribute belongs to the function on each device
+// and persists, so the runtime call is made once per (kernel, device, larger
+// size) on each thread; later launches find it in a thread-local record.
+hipError_t set_dynamic_lds(const void *kernel, size_t bytes);
+
 // ---------------------------------------------------------------- launchers
 // Each returns the HIP error of its launches (hipSuccess on success).  All
 // shapes are validated by the caller.

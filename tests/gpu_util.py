@@ -2,6 +2,7 @@
 around the C ABI (through the Python binding)."""
 from __future__ import annotations
 
+import math
 import sys
 
 import numpy as np
@@ -81,3 +82,31 @@ def values(cs_array, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return oracle.bf16_decode(cs_array)
     return np.asarray(cs_array, np.float64)
+
+
+def check_rows(got, ref, tol: float, label: str = "") -> float:
+    """Assert the whole-output relative L2 error and the error of every
+    (sequence, head) row are within tol.
+
+    A single wrong row barely moves the whole-output norm (one of b * heads
+    rows), so each row is held to the bound on its own.  A row is judged
+    against max(its own norm, a quarter of the RMS row norm), so that a row
+    whose reference nearly cancels (a near-uniform average of values) is not
+    held to a relative bound on a vanishing norm.  Returns the worst row error.
+    """
+    import oracle
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    whole = oracle.rel_l2(got, ref)
+    rows_g = got.reshape(-1, got.shape[-1])
+    rows_r = ref.reshape(-1, ref.shape[-1])
+    norms = np.linalg.norm(rows_r, axis=1)
+    floor = 0.25 * math.sqrt(float(np.mean(norms ** 2)))
+    errs = np.linalg.norm(rows_g - rows_r, axis=1) / np.maximum(norms, max(floor, 1e-300))
+    worst = int(np.argmax(errs))
+    say(f"  {label} rel-L2 {whole:.2e}, worst row {worst} {errs[worst]:.2e}")
+    assert whole <= tol, f"{label}: whole-output rel-L2 {whole:.3e} > {tol}"
+    assert errs[worst] <= tol, f"{label}: row {worst} (sequence {worst // got.shape[-2] if got.ndim > 2 else 0}) rel-L2 {errs[worst]:.3e} > {tol}"
+    return float(errs[worst])

@@ -105,6 +105,9 @@ def test_decode_validation():
     assert st_dec(b=65536) == -1                  # the batch fills a grid dimension
     assert st_dec(L=0) == -1
     assert st_dec(d=48) == -2
+    for d in (16, 32, 256):                       # the boundary takes d in {64, 128}
+        assert st_dec(d=d, heads=256 // d * 4 if d < 64 else 1, r=256) == -2, d
+    assert st_dec(cdt=q.F32, qdt=q.F32, wdt=q.F32, odt=q.F32, d=32, heads=8) == -2
     assert st_dec(r=100) == -1                    # bf16 cache needs r % 32
     assert st_dec(r=4096) == -2                   # beyond the per-wavefront budget
     assert st_dec(cdt=q.I4, cs=FAKE, cg=128, r=96) == -1   # int4 needs r % 128

@@ -4,7 +4,8 @@ chip, optional RoPE) against the float64 oracle attend_headwise.
 Inputs are synth.headwise_case bf16 bit patterns; the oracle consumes their
 exact values and computes its own RoPE angles in float64, while the kernel
 receives the float32 cos / sin tables a runtime would hand it.  Tolerance:
-relative L2 over the whole output <= 2e-2 (bf16 inputs, float32 MFMA
+relative L2 over the whole output, and of every (sequence, head) row in the
+shape sweep, <= 2e-2 (bf16 inputs, float32 MFMA
 accumulation, bf16 output; table rounding adds < 2^-24 relative per angle).
 """
 import numpy as np
@@ -12,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import dev, empty, host, say, values, workspace
+from gpu_util import check_rows, dev, empty, host, say, values, workspace
 
 import rank_latent_attention_amd as q
 
@@ -63,10 +64,7 @@ def test_headwise_matches_oracle(shape, rope):
     say(f"case: headwise b={b} L={L} heads={heads} rk={rk} rv={rv} rope={rope}")
     cs = synth.headwise_case(b, L, heads, 128, rk, rv, seed=L + heads)
     got = run_headwise(cs, rope)
-    assert np.all(np.isfinite(got))
-    err = oracle.rel_l2(got, oracle_out(cs, rope))
-    say(f"  rel-L2 {err:.2e}")
-    assert err <= TOL
+    check_rows(got, oracle_out(cs, rope), TOL, "headwise")
 
 
 @pytest.mark.parametrize("splits", [1, 3, 40])
