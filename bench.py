@@ -43,6 +43,7 @@ HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 COPY_BYTES = 1 << 30  # calibration copy (bytes read = bytes written)
+MALL_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 COUNTERS = os.path.join(ROOT, "profiles", "decode_stream_e4096_r1536_b16_l8192_counters.json")
 
 
@@ -57,11 +58,13 @@ def parse():
     # the clock climbs for ~20 ms of work after the idle input generation;
     # 200 decode steps (~22 ms) reach the steady state
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--copies", type=int, default=2, help="rotated cache copies")
+    ap.add_argument("--copies", type=int, default=2,
+                    help="minimum rotated cache copies (raised per leg to span 2 x 256 MiB)")
     ap.add_argument("--splits", type=int, default=0, help="L-splits (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--chain", action="store_true", help="also time the 24-layer prefill chain")
+    ap.add_argument("--no-chain", action="store_true", help="skip the 24-layer prefill chain")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny float32 latency leg")
     ap.add_argument("--no-explicit", action="store_true",
                     help="skip the explicit K/V reconstruction (RoPE) decode leg")
     ap.add_argument("--no-headwise", action="store_true",
@@ -82,18 +85,66 @@ def kernel_source_hash() -> str:
     return source_hash("decode.hip")
 
 
-def timed(fn, steps, warmup):
+def timed(fn, steps, warmup, stats=None):
+    """Mean milliseconds per call of fn over exactly `steps` calls after `warmup`
+    untimed ones, bracketed by synchronisations and a pair of HIP events on the
+    current stream.  With a dict `stats`, events at block boundaries (every
+    ~steps/10 calls, one marker per block) also give the median, p10 and p90 of
+    the per-call time over the blocks."""
+    import numpy as np
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        fn(i)
-    stop.record()
+    nblk = min(10, steps) if stats is not None else 1
+    bounds = [round(k * steps / nblk) for k in range(nblk + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
+    evs[0].record()
+    for k in range(nblk):
+        for i in range(bounds[k], bounds[k + 1]):
+            fn(i)
+        evs[k + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    if stats is not None:
+        per = np.array([evs[k].elapsed_time(evs[k + 1]) / (bounds[k + 1] - bounds[k]) for k in range(nblk)])
+        stats.update({"median_ms": round(float(np.median(per)), 5),
+                      "p10_ms": round(float(np.percentile(per, 10)), 5),
+                      "p90_ms": round(float(np.percentile(per, 90)), 5), "blocks": nblk})
+    return ms
+
+
+def kernel_times(q, torch, step, steps):
+    """Per-kernel launch times over `steps` calls of step, from the library's timing
+    session (one launch-boundary event before every kernel; a launch's time runs to
+    the next boundary, so the kernels of a step add up to the step).  Returns
+    ({kernel: mean ms per launch}, mean ms per step of this pass)."""
+    with q.timing(max_launches=8 * steps + 16) as tm:
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    kern = {k: v[1] / v[0] for k, v in tm.result.items()}
+    per_step = sum(v[1] for v in tm.result.values()) / steps
+    return kern, per_step
+
+
+def copies_for(working_set_bytes, requested):
+    """Cache copies rotated between steps: at least `requested`, and enough that the
+    copies together span twice the 256 MiB last-level cache, so that no step is served
+    from the previous step's lines."""
+    return max(requested, -(-2 * MALL_BYTES // max(int(working_set_bytes), 1)))
+
+
+def environment():
+    import torch
+    info = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+            "torch": torch.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    return info
 
 
 def main():
@@ -121,8 +172,10 @@ def main():
     cs = synth.config_decode_case(cfg)
     log(f"[bench] generated decode inputs ({cfg.name}) in {time.time() - t0:.1f}s")
     C0 = bf(cs.C)
-    copies = [C0] + [C0.clone() for _ in range(max(args.copies, 1) - 1)]
-    n_copies = len(copies)
+    cache_bytes = b * L * r * 2                       # one r-wide bf16 latent per cached token
+    step_bytes = cache_bytes + 2 * r * heads * d * 2 + 2 * b * heads * d * 2
+    n_copies = copies_for(step_bytes, args.copies)
+    copies = [C0] + [C0.clone() for _ in range(n_copies - 1)]
     qv, Wk, Wv = bf(cs.q), bf(cs.Wu_k), bf(cs.Wu_v)
     O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
     ws_bytes = q.qsvd_decode_workspace_bytes(b, L, r, heads, d, q.BF16, args.splits)
@@ -134,14 +187,12 @@ def main():
                            None, None, b, L, r, heads, d, cs.softmax_scale, args.splits, O,
                            q.BF16, ws, ws_bytes)
 
-    ms = timed(step, args.steps, args.warmup)
-    # per-kernel HIP-event times over a second pass of the same steps
-    with q.timing(max_launches=8 * args.steps + 16) as tm:
-        for i in range(args.steps):
-            step(i)
-    torch.cuda.synchronize()
-    kern = {k: v[1] / v[0] for k, v in tm.result.items()}
-    log(f"[bench] decode step {ms * 1e3:.1f} us; kernels (us): " +
+    step_stats = {}
+    ms = timed(step, args.steps, args.warmup, step_stats)
+    # per-kernel times: a pass of the same steps with a launch-boundary event per kernel
+    kern, kern_pass_ms = kernel_times(q, torch, step, args.steps)
+    log(f"[bench] decode step {ms * 1e3:.1f} us (median {step_stats['median_ms'] * 1e3:.1f}); "
+        f"kernel pass {kern_pass_ms * 1e3:.1f} us/step: " +
         ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kern.items()))
 
     # plain device copy of a known size: its FETCH_SIZE / WRITE_SIZE counters give the
@@ -153,8 +204,6 @@ def main():
     torch.cuda.synchronize()
     del src, dst
 
-    cache_bytes = b * L * r * 2                       # one r-wide bf16 latent per cached token
-    step_bytes = cache_bytes + 2 * r * heads * d * 2 + 2 * b * heads * d * 2
     stream_ms = kern.get("decode_stream", float("nan"))
     achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
     traffic = None
@@ -162,6 +211,11 @@ def main():
         c = json.load(open(COUNTERS))
         if c.get("decode_hip_sha256_16") == kernel_source_hash():
             traffic = c.get("hbm_bytes_per_launch")
+
+    # ------------------------------------------------------------------ tiny float32 latency leg
+    tiny = None
+    if not args.no_tiny:
+        tiny = tiny_leg(q, torch, synth, dev, args)
 
     # ------------------------------------------------------------------ explicit K/V leg
     explicit = None
@@ -250,7 +304,7 @@ def main():
                    "rotate_quant_c_us": round(t_a3 * 1e3, 2)}
         log(f"[bench] prefill: a1 {t_a1 * 1e3:.1f} us, a2 {t_a2 * 1e3:.1f} us ({tops:.0f} TOPS), "
             f"a3 {t_a3 * 1e3:.1f} us; W4A4 a2 {t_a2_4 * 1e3:.1f} us")
-        if args.chain:
+        if not args.no_chain:
             prefill["chain"] = chain_leg(q, torch, np, synth, xq, xs, M, E, steps=3)
         del Xd, xq, Cp, cq
 
@@ -278,12 +332,16 @@ def main():
                    "cache_copies": n_copies},
         "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_stats": step_stats,
         "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+        "kernel_pass_us_per_step": round(kern_pass_ms * 1e3, 2),
+        "environment": environment(),
         "roofline": {"bound": "hbm", "kernel": "decode_stream", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": cache_bytes},
         "cpu_baseline": cpu,
+        "tiny_fp32": tiny,
         "prefill": prefill,
         "explicit": explicit,
         "headwise": headwise,
@@ -329,7 +387,7 @@ def headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args, rk=64, rv=64):
     log(f"[bench] generated per-head latent inputs in {time.time() - t0:.1f}s")
     C0 = bf(hc.C)
     hc.C = None
-    copies = [C0] + [C0.clone() for _ in range(max(args.copies, 1) - 1)]
+    copies = [C0] + [C0.clone() for _ in range(copies_for(C0.numel() * 2, args.copies) - 1)]
     qv, BK, BV = bf(hc.q), bf(hc.BK_t), bf(hc.BV)
     rc, rs = (dev(t) for t in synth.rope_tables(L, d))
     O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
@@ -343,11 +401,8 @@ def headwise_leg(q, torch, synth, dev, bf, b, L, heads, d, args, rk=64, rv=64):
                                         tables[1], 0, O, q.BF16, ws)
         n = max(args.steps // 2, 5)
         ms = timed(step, n, args.warmup)
-        with q.timing(max_launches=4 * n + 8) as tm:
-            for i in range(n):
-                step(i)
-        torch.cuda.synchronize()
-        res[name] = (ms, {k: v[1] / v[0] for k, v in tm.result.items()})
+        kern, _ = kernel_times(q, torch, step, n)
+        res[name] = (ms, kern)
     cache_bytes = b * L * heads * (rk + rv) * 2
     ms, kern = res["rope"]
     stream_ms = kern.get("headwise_stream", float("nan"))
@@ -391,14 +446,14 @@ def counted_traffic(hash_key, source, kernels):
 
 
 def decode_timing(q, torch, step, args):
-    """Step time (HIP events around the timed steps) and per-kernel times (a second pass)."""
+    """Step time (HIP events around the timed steps, with block statistics) and
+    per-kernel launch times (a pass with launch-boundary events)."""
     n = max(args.steps // 2, 5)
-    ms = timed(step, n, args.warmup)
-    with q.timing(max_launches=8 * n + 16) as tm:
-        for i in range(n):
-            step(i)
-    torch.cuda.synchronize()
-    return ms, {k: v[1] / v[0] for k, v in tm.result.items()}
+    stats = {}
+    ms = timed(step, n, args.warmup, stats)
+    kern, pass_ms = kernel_times(q, torch, step, n)
+    stats["kernel_pass_us_per_step"] = round(pass_ms * 1e3, 2)
+    return ms, kern, stats
 
 
 def w8a4_leg(q, torch, np, synth, dev, bf, args):
@@ -414,8 +469,9 @@ def w8a4_leg(q, torch, np, synth, dev, bf, args):
     log(f"[bench] generated W8A4 decode inputs ({cfg.name}) in {time.time() - t0:.1f}s")
     M = b * L
     Cf = dev(cs.C.reshape(M, r))
+    cache_bytes = b * L * (r // 2 + 4 * (r // 128))
     copies = []
-    for _ in range(max(args.copies, 1)):
+    for _ in range(copies_for(cache_bytes, args.copies)):
         codes = torch.empty((M, r // 2), dtype=torch.uint8, device="cuda")
         scales = torch.empty((M, r // 128), dtype=torch.float32, device="cuda")
         q.qsvd_quantize_latent(Cf, q.F32, M, r, 0, q.I4, 128, codes, scales)
@@ -434,8 +490,8 @@ def w8a4_leg(q, torch, np, synth, dev, bf, args):
         q.qsvd_decode_attn(qv, q.BF16, codes, q.I4, scales, 128, Wk, Wv, q.I8, wsk, wsv, b, L, r,
                            heads, d, cs.softmax_scale, 0, O, q.BF16, ws)
 
-    ms, kern = decode_timing(q, torch, step, args)
-    cache_bytes = b * L * (r // 2 + 4 * (r // 128))
+    ms, kern, stats = decode_timing(q, torch, step, args)
+    n_copies = len(copies)
     stream_ms = kern.get("decode_stream", float("nan"))
     achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
     log(f"[bench] W8A4 decode: {ms * 1e3:.1f} us/step; kernels (us): " +
@@ -444,6 +500,7 @@ def w8a4_leg(q, torch, np, synth, dev, bf, args):
     return {"workload": f"decode step, {cfg.name}: int4 group-128 latent cache (codes + float32 "
                         "scales), int8 W^u with per-column scales",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(b / (ms * 1e-3), 1),
+            "cache_copies": n_copies, "step_stats": stats,
             "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
             "roofline": {"bound": "hbm", "kernel": "decode_stream", "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -463,7 +520,7 @@ def llava13b_leg(q, torch, synth, bf, args):
     log(f"[bench] generated 13B decode inputs ({cfg.name}) in {time.time() - t0:.1f}s")
     C0 = bf(cs.C)
     cs.C = None
-    copies = [C0] + [C0.clone() for _ in range(max(args.copies, 1) - 1)]
+    copies = [C0] + [C0.clone() for _ in range(copies_for(C0.numel() * 2, args.copies) - 1)]
     qv, Wk, Wv = bf(cs.q), bf(cs.Wu_k), bf(cs.Wu_v)
     O = torch.empty((b, heads, d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(q.qsvd_decode_workspace_bytes(b, L, r, heads, d, q.BF16, 0), dtype=torch.uint8,
@@ -473,7 +530,8 @@ def llava13b_leg(q, torch, synth, bf, args):
         q.qsvd_decode_attn(qv, q.BF16, copies[i % len(copies)], q.BF16, None, 0, Wk, Wv, q.BF16,
                            None, None, b, L, r, heads, d, cs.softmax_scale, 0, O, q.BF16, ws)
 
-    ms, kern = decode_timing(q, torch, step, args)
+    ms, kern, stats = decode_timing(q, torch, step, args)
+    n_copies = len(copies)
     cache_bytes = b * L * r * 2
     stream_ms = kern.get("decode_scores", float("nan")) + kern.get("decode_values", float("nan"))
     achieved = cache_bytes / (stream_ms * 1e-3) / 1e9
@@ -483,6 +541,7 @@ def llava13b_leg(q, torch, synth, bf, args):
     del copies, C0
     return {"workload": f"decode step, {cfg.name}: two-pass stream (decode_scores, decode_values)",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(b / (ms * 1e-3), 1),
+            "cache_copies": n_copies, "step_stats": stats,
             "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
             "pass_bytes_gbps": round(moved / (stream_ms * 1e-3) / 1e9, 1),
             "roofline": {"bound": "hbm", "kernel": "decode_scores + decode_values",
@@ -491,6 +550,39 @@ def llava13b_leg(q, torch, synth, bf, args):
                          "traffic": counted_traffic("decode_wide_hip_sha256_16", "decode_wide.hip",
                                                     ["wide_scores_kernel<3, 9>", "wide_values_kernel<3>"]),
                          "algorithmic_bytes": cache_bytes}}
+
+
+def tiny_leg(q, torch, synth, dev, args):
+    """Config 0, the tiny float32 layer (E = 256, 4 heads x 64, r = 96, b = 1, L = 512): a
+    latency figure.  Back-to-back steps give the device time per step; single calls each
+    followed by a synchronisation give the latency a caller sees (host launch included)."""
+    import numpy as np
+    cs = synth.config_decode_case(synth.CONFIGS[0])
+    qv, C, Wk, Wv = dev(cs.q), dev(cs.C), dev(cs.Wu_k), dev(cs.Wu_v)
+    O = torch.empty((cs.b, cs.heads, cs.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(q.qsvd_decode_workspace_bytes(cs.b, cs.L, cs.r, cs.heads, cs.d, q.F32, 0),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        q.qsvd_decode_attn(qv, q.F32, C, q.F32, None, 0, Wk, Wv, q.F32, None, None, cs.b, cs.L,
+                           cs.r, cs.heads, cs.d, cs.softmax_scale, 0, O, q.F32, ws)
+
+    ms = timed(step, max(args.steps, 20), max(args.warmup, 20))
+    kern, _ = kernel_times(q, torch, step, 20)
+    lat = []
+    for i in range(50):
+        t0 = time.perf_counter()
+        step(i)
+        torch.cuda.synchronize()
+        lat.append(time.perf_counter() - t0)
+    lat = np.array(lat) * 1e6
+    log(f"[bench] tiny fp32 decode: {ms * 1e3:.1f} us/step back to back, {np.median(lat):.1f} us "
+        "per synchronised call")
+    return {"workload": f"decode step, {synth.CONFIGS[0].name}", "us_per_step": round(ms * 1e3, 2),
+            "latency_us": {"median": round(float(np.median(lat)), 1),
+                           "p10": round(float(np.percentile(lat, 10)), 1),
+                           "p90": round(float(np.percentile(lat, 90)), 1)},
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()}}
 
 
 def dev_t(torch, np, a):

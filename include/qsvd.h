@@ -298,11 +298,15 @@ const char *qsvd_last_error(void);
 
 /*
  * Optional per-kernel timing on the calling thread.  Between
- * qsvd_timing_begin and qsvd_timing_end every kernel the library launches
- * from this thread is bracketed by a pair of HIP events recorded on the
- * stream it is launched on.  qsvd_timing_end waits for the last event and
- * returns, per kernel name, the launch count and the summed event time.
- * max_launches bounds the session (extra launches are not timed).
+ * qsvd_timing_begin and qsvd_timing_end the library records one HIP event on
+ * the launch stream just before every kernel it launches from this thread (a
+ * launch boundary).  A launch's time is the span from its boundary to the
+ * next boundary on the same stream, or to a closing event qsvd_timing_end
+ * records on that stream, so the times of a stream's launches add up to the
+ * session's span on it (idle gaps between launches are counted in the launch
+ * before the gap).  qsvd_timing_end waits for the closing events and returns,
+ * per kernel name, the launch count and the summed time.  max_launches bounds
+ * the session (extra launches are not timed).
  */
 typedef struct qsvd_kernel_time {
   char name[32];

@@ -46,9 +46,15 @@ const char *dtype_name(int dt) {
 }
 
 // ---------------------------------------------------------------- timing session
+// One event is recorded on the launch stream just before each timed launch
+// (a launch boundary).  A launch's time is the span from its boundary to the
+// next boundary on the same stream (or to the closing event qsvd_timing_end
+// records there), so the launch times of a stream add up to the whole span of
+// the session on it, idle gaps included, and each launch costs one marker.
 struct TimingRecord {
   const char *name;
-  hipEvent_t start, stop;
+  hipEvent_t start;
+  hipStream_t stream;
 };
 
 struct TimingSession {
@@ -64,19 +70,12 @@ thread_local TimingSession g_timing;
 
 namespace qsvd {
 
-LaunchTimer::LaunchTimer(const char *name, hipStream_t stream) : slot_(-1), stream_(stream) {
+LaunchTimer::LaunchTimer(const char *name, hipStream_t stream) {
   TimingSession &t = g_timing;
   if (!t.active || static_cast<int>(t.records.size()) >= t.max_launches) return;
-  const size_t i = t.records.size();
-  TimingRecord rec{name, t.pool[2 * i], t.pool[2 * i + 1]};
+  TimingRecord rec{name, t.pool[t.records.size()], stream};
   if (hipEventRecord(rec.start, stream) != hipSuccess) return;
   t.records.push_back(rec);
-  slot_ = static_cast<int>(i);
-}
-
-LaunchTimer::~LaunchTimer() {
-  if (slot_ < 0) return;
-  (void)hipEventRecord(g_timing.records[slot_].stop, stream_);
 }
 
 hipError_t set_dynamic_lds(const void *kernel, size_t bytes) {
@@ -390,6 +389,22 @@ qsvd_status_t qsvd_decode_attn_headwise(const void *q, qsvd_dtype_t q_dtype, con
                        "decode_attn_headwise");
 }
 
+namespace qsvd {
+
+// Validation and launch of one decode step (qsvd_decode_attn); workspace ==
+// nullptr with workspace_bytes == 0 only asks for the plan's size through
+// *need without launching (the arguments are still validated).
+qsvd_status_t decode_attn_checked(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                  qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
+                                  const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
+                                  const float *wu_scale_k, const float *wu_scale_v, int32_t b,
+                                  int64_t L, int32_t r, int32_t heads, int32_t d,
+                                  float softmax_scale, int32_t splits, void *O, qsvd_dtype_t o_dtype,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream,
+                                  size_t *need);
+
+}  // namespace qsvd
+
 qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *C,
                                qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
                                const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
@@ -397,6 +412,19 @@ qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *
                                int64_t L, int32_t r, int32_t heads, int32_t d,
                                float softmax_scale, int32_t splits, void *O, qsvd_dtype_t o_dtype,
                                void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return qsvd::decode_attn_checked(q, q_dtype, C, c_dtype, c_scales, c_group, Wu_k, Wu_v, wu_dtype,
+                                   wu_scale_k, wu_scale_v, b, L, r, heads, d, softmax_scale, splits,
+                                   O, o_dtype, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+qsvd_status_t qsvd::decode_attn_checked(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                        qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
+                                        const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
+                                        const float *wu_scale_k, const float *wu_scale_v, int32_t b,
+                                        int64_t L, int32_t r, int32_t heads, int32_t d,
+                                        float softmax_scale, int32_t splits, void *O,
+                                        qsvd_dtype_t o_dtype, void *workspace, size_t workspace_bytes,
+                                        void *hip_stream, size_t *need) {
   qsvd_status_t st = validate_decode_shape(b, L, r, heads, d, c_dtype, splits);
   if (st != QSVD_OK) return st;
   if (c_dtype == QSVD_F32) {
@@ -433,6 +461,10 @@ qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *
       (c_scales && !aligned4(c_scales)) || (workspace && !aligned16(workspace)))
     return fail(QSVD_ERR_INVALID, "decode: misaligned pointer");
   const qsvd::DecodePlan plan = qsvd::plan_decode(b, L, r, heads, d, c_dtype, splits);
+  if (need) {
+    *need = plan.total;
+    if (!workspace && workspace_bytes == 0) return ok();
+  }
   if (!workspace || workspace_bytes < plan.total)
     return fail(QSVD_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
                 plan.total);
@@ -467,7 +499,7 @@ qsvd_status_t qsvd_timing_begin(int32_t max_launches) {
   if (t.active) return fail(QSVD_ERR_INVALID, "timing_begin: a session is already active");
   if (max_launches < 1 || max_launches > (1 << 20))
     return fail(QSVD_ERR_INVALID, "timing_begin: max_launches = %d", max_launches);
-  t.pool.resize(static_cast<size_t>(2) * max_launches);
+  t.pool.resize(static_cast<size_t>(max_launches));
   for (auto &ev : t.pool) {
     const hipError_t e = hipEventCreate(&ev);
     if (e != hipSuccess) return device_status(e, "timing_begin");
@@ -484,12 +516,30 @@ qsvd_status_t qsvd_timing_end(qsvd_kernel_time_t *out, int32_t max_out, int32_t 
   if (!t.active) return fail(QSVD_ERR_INVALID, "timing_end: no active session");
   t.active = false;
   hipError_t err = hipSuccess;
-  std::vector<qsvd_kernel_time_t> agg;
-  if (!t.records.empty()) err = hipEventSynchronize(t.records.back().stop);
+  // closing boundary on every stream that has timed launches
+  std::vector<std::pair<hipStream_t, hipEvent_t>> closing;
   for (const auto &rec : t.records) {
+    bool seen = false;
+    for (auto &c : closing) seen = seen || c.first == rec.stream;
+    if (seen) continue;
+    hipEvent_t ev = nullptr;
+    err = hipEventCreate(&ev);
+    if (err == hipSuccess) err = hipEventRecord(ev, rec.stream);
+    if (err == hipSuccess) err = hipEventSynchronize(ev);
+    if (ev) closing.push_back({rec.stream, ev});
     if (err != hipSuccess) break;
+  }
+  std::vector<qsvd_kernel_time_t> agg;
+  const size_t n_rec = t.records.size();
+  for (size_t i = 0; i < n_rec && err == hipSuccess; ++i) {
+    const TimingRecord &rec = t.records[i];
+    hipEvent_t end = nullptr;
+    for (size_t j = i + 1; j < n_rec && !end; ++j)
+      if (t.records[j].stream == rec.stream) end = t.records[j].start;
+    for (auto &c : closing)
+      if (!end && c.first == rec.stream) end = c.second;
     float ms = 0.f;
-    err = hipEventElapsedTime(&ms, rec.start, rec.stop);
+    err = hipEventElapsedTime(&ms, rec.start, end);
     if (err != hipSuccess) break;
     qsvd_kernel_time_t *slot = nullptr;
     for (auto &a : agg)
@@ -503,6 +553,7 @@ qsvd_status_t qsvd_timing_end(qsvd_kernel_time_t *out, int32_t max_out, int32_t 
     slot->launches += 1;
     slot->total_ms += ms;
   }
+  for (auto &c : closing) (void)hipEventDestroy(c.second);
   for (auto &ev : t.pool) (void)hipEventDestroy(ev);
   t.pool.clear();
   t.records.clear();

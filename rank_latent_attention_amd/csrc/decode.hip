@@ -156,12 +156,17 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
   for (int k = 0; k < DK; ++k) {
     const int i = 32 * k + kq;
     u32x4 a = av[k], w = bv[k];
+    // int8 W^u_k: q times the column scales, carried as a bf16 pair
+    // (head + tail, about 16 significant bits) so that the product keeps
+    // the precision of q itself
+    u32x4 a_tail = {0u, 0u, 0u, 0u};
     if (wscale) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = __uint_as_float(a[e] << 16) * wscale[h * d + i + 2 * e];
         const float hi = __uint_as_float(a[e] & 0xFFFF0000u) * wscale[h * d + i + 2 * e + 1];
         a[e] = pack_bf16x2(lo, hi);
+        a_tail[e] = pack_bf16x2(lo - __uint_as_float(a[e] << 16), hi - __uint_as_float(a[e] & 0xFFFF0000u));
       }
     }
     if constexpr (sizeof(WT) == 1) {
@@ -177,6 +182,9 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
     // lane ends with 4 consecutive rows j0 + 4 g + (0..3) of sequence b0 + i
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                   __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
+    if (wscale)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                    __builtin_bit_cast(bf16x8, a_tail), acc, 0, 0, 0);
   }
   const int jo = j0 + 4 * (lane >> 4);
   if (bb < b && jo < r)  // r % 16 == 0: the 4 rows are all valid
@@ -303,11 +311,25 @@ __host__ __device__ constexpr int ct_row_stride(int nkb) { return nkb * 64 + 16;
 // padded so that the 16 heads of one store land in distinct LDS banks)
 __host__ __device__ constexpr int sp_row(int T) { return T + 4; }
 
-// LDS bytes of the stream kernel: wavefront C tiles | partial scores | P | alpha, m, l.
-__host__ __device__ constexpr size_t stream_lds_bytes(int W, int NHB, int NKB, int T) {
+// Scale groups of one wavefront's columns: int4 caches carry one scale per
+// 128-column group (NKB / 4 groups per wavefront, whose columns are whole
+// groups); int8 caches one scale per token.
+__host__ __device__ constexpr int stream_groups(bool int4, int NKB) { return int4 ? NKB / 4 : 1; }
+
+// Quantised 64-token tiles: depths (tiles of loads in flight) whose staging
+// registers fit beside O~ and Q~ without spilling (checked in the gfx950
+// assembly of each instantiation).
+__host__ __device__ constexpr bool stream_depth_fits(bool int4, int NHB, int NKB, int D) {
+  return D == 1 || (D == 2 && (int4 ? NKB <= 4 : NKB * NHB <= 4)) || (D == 3 && int4 && NKB <= 4 && NHB == 1);
+}
+
+// LDS bytes of the stream kernel: wavefront C tiles | partial scores | P |
+// alpha, m, l | (quantised caches) each wavefront's scales of the tile.
+__host__ __device__ constexpr size_t stream_lds_bytes(int W, int NHB, int NKB, int T, int c_kind = 0) {
   return static_cast<size_t>(W) * T * ct_row_stride(NKB) +
          static_cast<size_t>(W) * NHB * 16 * sp_row(T) * 4 + static_cast<size_t>(NHB) * 64 * T / 2 +
-         static_cast<size_t>(NHB) * 16 * 4 * 3;
+         static_cast<size_t>(NHB) * 16 * 4 * 3 +
+         (c_kind == 0 ? 0 : static_cast<size_t>(W) * stream_groups(c_kind == 1, NKB) * T * 4);
 }
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t *p) {
@@ -326,10 +348,40 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// bf16 pair of two dequantised codes c * s (float32 product, round to nearest even).
-__device__ __forceinline__ uint32_t dq_pair(int c0, int c1, float s) {
-  return cvt_bf16x2(static_cast<float>(c0) * s, static_cast<float>(c1) * s);
+// Exact integer codes as bf16 MFMA operands, offset by a constant so that the
+// conversion is a few bit operations per code (the scales are applied to the
+// products instead, see stream_mfma_kernel).
+//
+// int4: the bf16 bit pattern 0x4300 | m is the value 128 + m for a 7-bit m,
+// and m = n ^ 8 maps the two's-complement nibble n of a code c to c + 8, so
+// 0x4300 | (n ^ 8) is exactly 136 + c.  One dword holds codes n0..n7 (n0 in
+// the lowest nibble); the four output dwords hold the pairs (n0, n4),
+// (n1, n5), (n2, n6), (n3, n7), i.e. K position p carries code
+// kI4Perm[p] of the group of eight.
+constexpr float kI4Offset = 136.f;
+constexpr float kI8Offset = 128.f;
+__device__ __forceinline__ u32x4 i4_codes_bf16(uint32_t w) {
+  // (n ^ 8) | 0x4300 == n ^ 0x4308 for a nibble n: one and-xor per pair
+  const uint32_t m = 0x000F000Fu, e = 0x43084308u;
+  return u32x4{(w & m) ^ e, ((w >> 4) & m) ^ e, ((w >> 8) & m) ^ e, ((w >> 12) & m) ^ e};
 }
+// int8: c ^ 0x80 is the unsigned byte c + 128, converted exactly by
+// v_cvt_f32_ubyteN; bf16 keeps the upper half of an integer below 256 exactly.
+__device__ __forceinline__ u32x2 i8_codes_bf16(uint32_t w) {
+  const uint32_t x = w ^ 0x80808080u;
+  const float f0 = static_cast<float>(x & 0xFFu), f1 = static_cast<float>((x >> 8) & 0xFFu);
+  const float f2 = static_cast<float>((x >> 16) & 0xFFu), f3 = static_cast<float>(x >> 24);
+  return u32x2{__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u),
+               __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u)};
+}
+// The int4 K order applied to eight consecutive bf16 values (q0..q7 in
+// v[0..3] as pairs): (q0, q4), (q1, q5), (q2, q6), (q3, q7).
+__device__ __forceinline__ u32x4 i4_order(u32x4 v) {
+  return u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+               __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+}
+// Column (within its group of eight) held at K position p of the int4 order.
+__device__ __forceinline__ int i4_column(int p) { return (p >> 1) + 4 * (p & 1); }
 
 // Reductions over aligned groups of N = 8 or 16 lanes with DPP lane swaps
 // (xor 1, xor 2, mirror within 8, mirror within 16).
@@ -380,7 +432,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   constexpr int MAXW = 8;
   static_assert(NKB % KPL == 0, "wavefront columns must be whole 16-byte loads");
   static_assert(T == 16 || T == 32 || T == 64, "tile");
-  static_assert(D == 1 || D == 2, "prefetch depth");
+  static_assert(D >= 1 && D <= 4, "prefetch depth");
   static_assert(HGP * RW * 2 <= T * RS, "the output rows are staged in the wavefront's C tile");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -418,6 +470,8 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   float *alpha_s = reinterpret_cast<float *>(pl + NHB * 64 * (T / 4));
   float *m_s = alpha_s + HGP;
   float *l_s = m_s + HGP;
+  // quantised caches: this wavefront's scales of the tile, [group][token]
+  float *ssc = l_s + HGP + static_cast<size_t>(wave) * stream_groups(CT == CT_I4, NKB) * T;
 
   // ---- tile loads through buffer resources based at the tile's first row:
   // rows at or past the end of the sequence fall outside the resource and
@@ -451,15 +505,18 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   };
   auto tile_start = [&](int it) { return (static_cast<int64_t>(split) + static_cast<int64_t>(it) * p.S) * T; };
 
-  // the first D tiles are requested before anything else
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb)
-    if (ntiles > 0) load_rows(std::integral_constant<int, 0>{}, tile_start(0), tb);
-  if constexpr (D == 2) {
+  // the first D tiles are requested before anything else (buffer k holds
+  // tiles k, k + D, k + 2 D, ...)
+  auto prefetch = [&](auto BUF) {
+    constexpr int k = decltype(BUF)::value;
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
-      if (ntiles > 1) load_rows(std::integral_constant<int, D - 1>{}, tile_start(1), tb);
-  }
+      if (ntiles > k) load_rows(BUF, tile_start(k), tb);
+  };
+  prefetch(std::integral_constant<int, 0>{});
+  if constexpr (D > 1) prefetch(std::integral_constant<int, 1>{});
+  if constexpr (D > 2) prefetch(std::integral_constant<int, 2>{});
+  if constexpr (D > 3) prefetch(std::integral_constant<int, 3>{});
 
   // Absorbed queries as the B operand of the score product.  K block
   // kb = KPL * ld + s of lane group g covers columns
@@ -477,10 +534,42 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         const int j = j0w + 32 * KPL * ld + EPL * lg + 8 * s;
         v = *reinterpret_cast<const u32x4 *>(p.qt + (static_cast<int64_t>(seq) * p.heads + h0 + h) * r + j);
       }
+      if constexpr (CT == CT_I4) v = i4_order(v);   // the K order of the int4 code operands
       qf[hb][kb] = __builtin_bit_cast(bf16x8, v);
     }
 
+  // Quantised caches: the score and value products run on the exact codes
+  // plus a constant offset (136 for int4, 128 for int8) and the scales are
+  // applied to the results.  For a wavefront and scale group g:
+  //   partial score  s_t = scale_{t,g} (sum_j (off + c_tj) q~_j - off sum_j q~_j)
+  //   value product  O~_j = sum_t P'_t (off + c_tj) - off sum_t P'_t,
+  //                  P'_t = bf16(p_t scale_{t,g})
+  // koff holds off * sum_j q~_j (a product of ones with the Q~ operands) and
+  // psum the running sum of the P' this lane contributes (rescaled with O~).
+  constexpr int NG = stream_groups(CT == CT_I4, NKB);
+  constexpr float kOff = CT == CT_I4 ? kI4Offset : kI8Offset;
+  constexpr int KPG = NKB / NG;       // K blocks per scale group
+  float koff[NG][NHB];
+  f32x4 psum[NG][NHB];   // sum_t P'_t of head 16 hb + i (all four elements), from MFMAs
+  if constexpr (CT != CT_BF16) {
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = g * KPG; kb < (g + 1) * KPG; ++kb)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, qf[hb][kb], a, 0, 0, 0);
+        koff[g][hb] = kOff * a[0];
+        psum[g][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  }
+  const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const bf16x4 ones4 = __builtin_bit_cast(bf16x4, u32x2{0x3F803F80u, 0x3F803F80u});
+
   // O~ transposed: oacc[hb][jb] holds columns 16 jb + 4 g + (0..3) of head 16 hb + i
+  // (K positions of the int4 order for int4 caches)
   f32x4 oacc[NHB][NJB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
@@ -496,6 +585,8 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   auto body = [&](auto BUF, int it) {
     constexpr int bf = decltype(BUF)::value;
     const int64_t tile_t0 = tile_start(it);
+    // tokens of this tile inside the sequence (wave-uniform)
+    const int tile_valid = static_cast<int>(std::min<int64_t>(L - tile_t0, T));
     const bool more = it + D < ntiles;
     const int64_t next_t0 = tile_start(it + D);
 
@@ -511,39 +602,34 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         } else if constexpr (CT == CT_I8) {
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            uint32_t o[4];
-#pragma unroll
-            for (int w2 = 0; w2 < 2; ++w2) {
-              const uint32_t word = stage[bf][tb][ld][2 * s + w2];
-              o[2 * w2] = dq_pair(static_cast<int>(word << 24) >> 24,
-                                  static_cast<int>(word << 16) >> 24, sscale[bf][tb][ld]);
-              o[2 * w2 + 1] = dq_pair(static_cast<int>(word << 8) >> 24,
-                                      static_cast<int>(word) >> 24, sscale[bf][tb][ld]);
-            }
-            cv[2 * ld + s] = u32x4{o[0], o[1], o[2], o[3]};
+            const u32x2 a = i8_codes_bf16(stage[bf][tb][ld][2 * s]);
+            const u32x2 c = i8_codes_bf16(stage[bf][tb][ld][2 * s + 1]);
+            cv[2 * ld + s] = u32x4{a.x, a.y, c.x, c.y};
           }
         } else {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const uint32_t word = stage[bf][tb][ld][s];
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              o[e] = dq_pair(static_cast<int>(word << (28 - 8 * e)) >> 28,
-                             static_cast<int>(word << (24 - 8 * e)) >> 28, sscale[bf][tb][ld]);
-            cv[4 * ld + s] = u32x4{o[0], o[1], o[2], o[3]};
-          }
+          for (int s = 0; s < 4; ++s) cv[4 * ld + s] = i4_codes_bf16(stage[bf][tb][ld][s]);
         }
       }
-      f32x4 sacc[NHB];
+      if constexpr (CT != CT_BF16) {
+        // the scales of token 16 tb + li (one per group) for the folds below;
+        // same-wavefront LDS write -> read, ordered by the LDS queue
+        if (lg == 0) {
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int g = 0; g < NG; ++g) ssc[g * T + tb * 16 + li] = sscale[bf][tb][g * (NLD / NG)];
+        }
+      }
+      f32x4 sacc[NG][NHB];
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) sacc[g][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb)
-          sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, cv[kb]), qf[hb][kb], sacc[hb], 0, 0, 0);
+          sacc[kb / KPG][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, cv[kb]), qf[hb][kb], sacc[kb / KPG][hb], 0, 0, 0);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int ld = kb / KPL, s = kb % KPL;
@@ -552,44 +638,97 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       }
       if (more) load_rows(BUF, next_t0, tb);
       // partial scores, head-major: lane holds tokens 16 tb + 4 g + (0..3) of head 16 hb + i
+      f32x4 part[NHB];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) part[hb] = sacc[0][hb];
+      if constexpr (CT != CT_BF16) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const f32x4 s4 = *reinterpret_cast<const f32x4 *>(ssc + g * T + tb * 16 + 4 * lg);
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = (sacc[g][hb][e] - koff[g][hb]) * s4[e];
+              part[hb][e] = g == 0 ? v : part[hb][e] + v;
+            }
+        }
+      }
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        *reinterpret_cast<f32x4 *>(spart + (wave * HGP + hb * 16 + li) * SPR + tb * 16 + 4 * lg) = sacc[hb];
+        *reinterpret_cast<f32x4 *>(spart + (wave * HGP + hb * 16 + li) * SPR + tb * 16 + 4 * lg) = part[hb];
     }
     lds_barrier();   // the next tile's loads stay in flight
 
-    // ---- 4. cross-wavefront sum + online softmax; T/2 lanes per head, 2 tokens each
-    for (int item = tid; item < HGP * (T / 2); item += nthreads) {
-      const int h = item / (T / 2), u = item % (T / 2), t0 = 2 * u;
-      float s0 = 0.f, s1 = 0.f;
-      // all MAXW reads in flight: rows past W re-read row W-1 and add nothing
-      float2 v[MAXW];
+    // ---- 4. cross-wavefront sum + online softmax: 8 lanes per head, TPI =
+    // T / 8 consecutive tokens each (the max and the sum are per-lane over
+    // the tokens, then 3 DPP steps over the head's 8 lanes)
+    {
+      constexpr int TPI = T / 8;
+      for (int item = tid; item < HGP * 8; item += nthreads) {
+        const int h = item >> 3, u = item & 7, t0 = u * TPI;
+        // rows past W are not read (wave-uniform bound, constant row offsets)
+        const float *sph = spart + h * SPR + t0;
+        float sc[TPI];
 #pragma unroll
-      for (int w = 0; w < MAXW; ++w)
-        v[w] = *reinterpret_cast<const float2 *>(spart + (min(w, W - 1) * HGP + h) * SPR + t0);
+        for (int w = 0; w < MAXW; ++w) {
+          if (w < W) {
+            float v[TPI];
+            if constexpr (TPI == 8) {
+              const f32x4 a = *reinterpret_cast<const f32x4 *>(sph + w * (HGP * SPR));
+              const f32x4 c = *reinterpret_cast<const f32x4 *>(sph + w * (HGP * SPR) + 4);
 #pragma unroll
-      for (int w = 0; w < MAXW; ++w) {
-        s0 += (w < W) ? v[w].x : 0.f;
-        s1 += (w < W) ? v[w].y : 0.f;
+              for (int e = 0; e < 4; ++e) {
+                v[e] = a[e];
+                v[4 + e] = c[e];
+              }
+            } else if constexpr (TPI == 4) {
+              const f32x4 a = *reinterpret_cast<const f32x4 *>(sph + w * (HGP * SPR));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = a[e];
+            } else {
+              const float2 a = *reinterpret_cast<const float2 *>(sph + w * (HGP * SPR));
+              v[0] = a.x;
+              v[1] = a.y;
+            }
+#pragma unroll
+            for (int e = 0; e < TPI; ++e) sc[e] = w == 0 ? v[e] : sc[e] + v[e];
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < TPI; ++e) {
+          if (t0 + e >= tile_valid) sc[e] = -INFINITY;
+          mx = fmaxf(mx, sc[e]);
+        }
+        mx = dpp_reduce<8, true>(mx);
+        const float m_old = m_s[h];
+        const float m_new = fmaxf(m_old, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
+        uint32_t pp[TPI / 2];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < TPI / 2; ++e) {
+          pp[e] = cvt_bf16x2(__builtin_amdgcn_exp2f(sc[2 * e] - m_new), __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_new));
+          ps += __uint_as_float(pp[e] << 16) + __uint_as_float(pp[e] & 0xFFFF0000u);
+        }
+        ps = dpp_reduce<8, false>(ps);
+        if (u == 0) {
+          m_s[h] = m_new;
+          l_s[h] = fmaf(l_s[h], alpha, ps);
+          alpha_s[h] = alpha;
+        }
+        // P as the B operand of the value product: K step t / 32 (T >= 32), lane
+        // 16 ((t % 32) / PPL) + h % 16, element t % PPL (TPI <= PPL, aligned)
+        const int ks = T == 16 ? 0 : t0 >> 5, tk = T == 16 ? t0 : t0 & 31;
+        uint16_t *pdst = pl + ((ks * NHB + (h >> 4)) * 64 + 16 * (tk / PPL) + (h & 15)) * PPL + (tk % PPL);
+        if constexpr (TPI == 8)
+          *reinterpret_cast<u32x4 *>(pdst) = u32x4{pp[0], pp[1], pp[2], pp[3]};
+        else if constexpr (TPI == 4)
+          *reinterpret_cast<u32x2 *>(pdst) = u32x2{pp[0], pp[1]};
+        else
+          *reinterpret_cast<uint32_t *>(pdst) = pp[0];
       }
-      if (tile_t0 + t0 >= L) s0 = -INFINITY;
-      if (tile_t0 + t0 + 1 >= L) s1 = -INFINITY;
-      const float mx = dpp_reduce<T / 2, true>(fmaxf(s0, s1));
-      const float m_old = m_s[h];
-      const float m_new = fmaxf(m_old, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
-      const uint32_t pp = cvt_bf16x2(__builtin_amdgcn_exp2f(s0 - m_new), __builtin_amdgcn_exp2f(s1 - m_new));
-      const float psum = dpp_reduce<T / 2, false>(__uint_as_float(pp << 16) + __uint_as_float(pp & 0xFFFF0000u));
-      if (u == 0) {
-        m_s[h] = m_new;
-        l_s[h] = fmaf(l_s[h], alpha, psum);
-        alpha_s[h] = alpha;
-      }
-      // P as the B operand of the value product: K step t / 32 (T >= 32), lane
-      // 16 ((t % 32) / PPL) + h % 16, element t % PPL
-      const int ks = T == 16 ? 0 : t0 >> 5, tk = T == 16 ? t0 : t0 & 31;
-      uint16_t *pdst = pl + ((ks * NHB + (h >> 4)) * 64 + 16 * (tk / PPL) + (h & 15)) * PPL + (tk % PPL);
-      *reinterpret_cast<uint32_t *>(pdst) = pp;
     }
     lds_barrier();
 
@@ -603,6 +742,10 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) oacc[hb][jb][e] *= al;
+        if constexpr (CT != CT_BF16) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) psum[g][hb][0] *= al;
+        }
       }
     }
     // A operand: column 16 jb + lane % 16, tokens PPL g + (0..PPL-1), by
@@ -613,15 +756,36 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
      for (int ks = 0; ks < NKS; ++ks) {
       // K step ks: tokens 32 ks + PPL g + (0..PPL-1)
       const uint8_t *trb = ct + (32 * ks + PPL * lg + (li >> 2)) * RS + (4 * (li & 3)) * 2;
-      bf16x8 pb[NHB];
+      // P of this lane's tokens (head 16 hb + li); quantised caches scale it
+      // per group: P'_g = bf16(p scale_{t,g})
+      bf16x8 pq[NG][NHB];
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
-        pb[hb] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4 *>(pl + ((ks * NHB + hb) * 64 + lane) * PPL));
+      for (int hb = 0; hb < NHB; ++hb) {
+        const u32x4 pv = *reinterpret_cast<const u32x4 *>(pl + ((ks * NHB + hb) * 64 + lane) * PPL);
+        if constexpr (CT == CT_BF16) {
+          pq[0][hb] = __builtin_bit_cast(bf16x8, pv);
+        } else {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const f32x4 sa = *reinterpret_cast<const f32x4 *>(ssc + g * T + 32 * ks + PPL * lg);
+            const f32x4 sb = *reinterpret_cast<const f32x4 *>(ssc + g * T + 32 * ks + PPL * lg + 4);
+            u32x4 q;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float s_lo = i < 2 ? sa[2 * i] : sb[2 * i - 4];
+              const float s_hi = i < 2 ? sa[2 * i + 1] : sb[2 * i - 3];
+              q[i] = cvt_bf16x2(__uint_as_float(pv[i] << 16) * s_lo, __uint_as_float(pv[i] & 0xFFFF0000u) * s_hi);
+            }
+            pq[g][hb] = __builtin_bit_cast(bf16x8, q);
+            // sum over the tokens of the P' the products use (ones as A)
+            psum[g][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pq[g][hb], psum[g][hb], 0, 0, 0);
+          }
+        }
+      }
       // column blocks in groups of VB: all transposing reads of a group are
-      // issued before its products
+      // issued before its products (a group never straddles two scale groups)
       constexpr int VB = (NJB % 4 == 0) ? 4 : ((NJB % 3 == 0) ? 3 : 2);
-      static_assert(NJB % VB == 0, "column groups");
+      static_assert(NJB % VB == 0 && (NJB / NG) % VB == 0, "column groups");
 #pragma unroll
       for (int jg = 0; jg < NJB; jg += VB) {
         bf16x4 lo[VB], hi[VB];
@@ -635,18 +799,35 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
           const bf16x8 av = __builtin_shufflevector(lo[k], hi[k], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb)
-            oacc[hb][jg + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hb], oacc[hb][jg + k], 0, 0, 0);
+            oacc[hb][jg + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pq[jg / (NJB / NG)][hb],
+                                                                      oacc[hb][jg + k], 0, 0, 0);
         }
       }
      }
     } else {
       const uint8_t *trb = ct + (PPL * lg + (li >> 2)) * RS + (4 * (li & 3)) * 2;
-      bf16x4 pb[NHB];
+      bf16x4 pq[NG][NHB];
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
-        pb[hb] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(pl + (hb * 64 + lane) * PPL));
+      for (int hb = 0; hb < NHB; ++hb) {
+        const u32x2 pv = *reinterpret_cast<const u32x2 *>(pl + (hb * 64 + lane) * PPL);
+        if constexpr (CT == CT_BF16) {
+          pq[0][hb] = __builtin_bit_cast(bf16x4, pv);
+        } else {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const f32x4 sa = *reinterpret_cast<const f32x4 *>(ssc + g * T + PPL * lg);
+            u32x2 q;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              q[i] = cvt_bf16x2(__uint_as_float(pv[i] << 16) * sa[2 * i],
+                                __uint_as_float(pv[i] & 0xFFFF0000u) * sa[2 * i + 1]);
+            pq[g][hb] = __builtin_bit_cast(bf16x4, q);
+            psum[g][hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pq[g][hb], psum[g][hb], 0, 0, 0);
+          }
+        }
+      }
       constexpr int VB = (NJB % 4 == 0) ? 4 : ((NJB % 3 == 0) ? 3 : 2);
-      static_assert(NJB % VB == 0, "column groups");
+      static_assert(NJB % VB == 0 && (NJB / NG) % VB == 0, "column groups");
 #pragma unroll
       for (int jg = 0; jg < NJB; jg += VB) {
         bf16x4 av[VB];
@@ -656,15 +837,22 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         for (int k = 0; k < VB; ++k)
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb)
-            oacc[hb][jg + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[k], pb[hb], oacc[hb][jg + k], 0, 0, 0);
+            oacc[hb][jg + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[k], pq[jg / (NJB / NG)][hb],
+                                                                        oacc[hb][jg + k], 0, 0, 0);
       }
     }
   };
 
   for (int it = 0; it < ntiles; it += D) {
     body(std::integral_constant<int, 0>{}, it);
-    if constexpr (D == 2) {
+    if constexpr (D > 1) {
       if (it + 1 < ntiles) body(std::integral_constant<int, 1>{}, it + 1);
+    }
+    if constexpr (D > 2) {
+      if (it + 2 < ntiles) body(std::integral_constant<int, 2>{}, it + 2);
+    }
+    if constexpr (D > 3) {
+      if (it + 3 < ntiles) body(std::integral_constant<int, 3>{}, it + 3);
     }
   }
   __syncthreads();
@@ -680,11 +868,36 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       const int h = hb * 16 + li;
       const float l = l_s[h];
       const float inv = l > 0.f ? 1.f / l : 0.f;
+      float corr[NG];   // quantised caches: off * sum_t P'_t over the four lanes of head h
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb)
-        *reinterpret_cast<u32x2 *>(ot + h * RW + jb * 16 + 4 * lg) =
-            u32x2{cvt_bf16x2(oacc[hb][jb][0] * inv, oacc[hb][jb][1] * inv),
-                  cvt_bf16x2(oacc[hb][jb][2] * inv, oacc[hb][jb][3] * inv)};
+      for (int g = 0; g < NG; ++g) {
+        corr[g] = 0.f;
+        if constexpr (CT != CT_BF16) corr[g] = kOff * psum[g][hb][0];
+      }
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        f32x4 o = oacc[hb][jb];
+        if constexpr (CT != CT_BF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (o[e] - corr[jb / (NJB / NG)]) * inv;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] *= inv;
+        }
+        if constexpr (CT == CT_I4) {
+          // K positions 16 jb + 4 g + e of the int4 order back to columns
+          uint16_t *row = ot + h * RW + jb * 16 + 8 * (lg >> 1);
+          const int p0 = 4 * (lg & 1);
+          const uint32_t a = cvt_bf16x2(o[0], o[1]), c = cvt_bf16x2(o[2], o[3]);
+          row[i4_column(p0)] = static_cast<uint16_t>(a);
+          row[i4_column(p0 + 1)] = static_cast<uint16_t>(a >> 16);
+          row[i4_column(p0 + 2)] = static_cast<uint16_t>(c);
+          row[i4_column(p0 + 3)] = static_cast<uint16_t>(c >> 16);
+        } else {
+          *reinterpret_cast<u32x2 *>(ot + h * RW + jb * 16 + 4 * lg) =
+              u32x2{cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3])};
+        }
+      }
     }
     // same-wavefront LDS write -> read, ordered by the LDS queue; the partials
     // stream out with non-temporal stores (written once, read once by the merge)
@@ -700,51 +913,61 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
 }
 
 // ------------------------------------------------------------------ MFMA merge
-// Workgroup (chunk jc of kMergeRows latent rows, head h, 16 sequences).  All
-// global loads are issued up front (one memory round trip):
-//   - the chunk of W^u_v,h (kMergeRows x d) into registers (int8 codes are
-//     exact in bf16; their column scales multiply the result);
-//   - (m, l) of every split (thread = sequence tid / 16, splits tid % 16 + 16 k);
+// Workgroup (chunk jc of MR latent rows, head h, 16 sequences), 512 threads;
+// the host picks MR so that the grid is (about) one round of the compute
+// units.  All global loads are issued up front (one memory round trip):
+//   - the chunk of W^u_v,h (MR x d) into registers (int8 codes are exact in
+//     bf16; their column scales multiply the result);
+//   - (m, l) of every split (threads 0..255: sequence tid / 16, splits
+//     tid % 16 + 16 k);
 //   - the partial O~ rows of up to kMergeBatch splits (thread = sequence
-//     tid / 16, rows 8 (tid % 16) .. +8).
+//     tid / (MR / 8), rows 8 (tid % (MR / 8)) .. +8).
 // Then: log-sum-exp weights (16-lane DPP reductions), the merged O~ rows as
 // the A operand of v_mfma_f32_16x16x32_bf16 (M = 16 sequences, K = latent
 // rows) in LDS, the W chunk to LDS, and O~ W^u_v,h with the B operand read by
 // transposing LDS loads -> opj[jc][b][h][:] (float32), summed over the chunks
 // by decode_finalize.  W^u_v is read once per (chunk, head, 16 sequences).
 constexpr int kMergeBatch = 16;
+constexpr int kMergeThreads = 512;
 
-template <typename WT>
-__global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restrict__ opart,
-                                                         const float *__restrict__ ml,
-                                                         const WT *__restrict__ Wv,
-                                                         const float *__restrict__ wscale,
-                                                         float *__restrict__ opj, int b, int r,
-                                                         int heads, int d, int S, int RW) {
+template <typename WT, int MR>
+__global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(const uint16_t *__restrict__ opart,
+                                                                   const float *__restrict__ ml,
+                                                                   const WT *__restrict__ Wv,
+                                                                   const float *__restrict__ wscale,
+                                                                   float *__restrict__ opj, int b, int r,
+                                                                   int heads, int d, int S, int RW) {
   constexpr int BB = 16;
-  constexpr int MAXU = kMergeRows * 256 / 8 / 256;  // 8-column W units per thread (d <= 256)
-  constexpr int MAXSL = 4;                          // splits per thread held in registers (S <= 64)
+  constexpr int NT = kMergeThreads;
+  constexpr int OCT = MR / 8;                       // 8-row groups of the chunk
+  constexpr int MAXU = (MR * 16 + NT - 1) / NT;     // 8-column W units per thread (d <= 128)
+  constexpr int MAXSL = 4;                          // splits per thread held in registers
+  static_assert(MR % 32 == 0 && BB * OCT <= NT, "merge chunk");
   extern __shared__ __attribute__((aligned(16))) uint8_t msm[];
-  const int WRS = d * 2 + 16;                                       // W chunk row stride (bytes)
-  uint8_t *wl = msm;                                                // [kMergeRows][WRS]
-  u32x4 *aop = reinterpret_cast<u32x4 *>(msm + kMergeRows * WRS);   // [kMergeRows/32][64]
-  float *wts = reinterpret_cast<float *>(aop + (kMergeRows / 32) * 64);  // [BB][S]
+  const int WRS = d * 2 + 16;                                  // W chunk row stride (bytes)
+  uint8_t *wl = msm;                                           // [MR][WRS]
+  u32x4 *aop = reinterpret_cast<u32x4 *>(msm + MR * WRS);      // [MR/32][64]
+  float *wts = reinterpret_cast<float *>(aop + (MR / 32) * 64);  // [BB][S]
   const int jc = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * BB;
   const int nbb = min(BB, b - b0);
   const int64_t E = static_cast<int64_t>(heads) * d;
-  const int j0 = jc * kMergeRows;
-  const int rows = min(kMergeRows, r - j0);  // multiple of 32
+  const int j0 = jc * MR;
+  const int rows = min(MR, r - j0);  // multiple of 32
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int units = d / 8;                   // 8-column units per row
-  const int bi = tid >> 4, sl = tid & 15, jj0 = sl * 8;
-  const int bseq = b0 + min(bi, nbb - 1);
-  const bool rvalid = bi < nbb && jj0 < rows;
+  const int units = d / 8;           // 8-column units per row
+  // partial-row role
+  const int pbi = tid / OCT, poc = tid % OCT, jj0 = poc * 8;
+  const bool rvalid = pbi < nbb && jj0 < rows;
+  const int pseq = b0 + min(pbi, nbb - 1);
+  // split-weight role (threads 0..255)
+  const int wbi = (tid >> 4) & 15, sl = tid & 15;
+  const int wseq = b0 + min(wbi, nbb - 1);
 
   // ---- all loads
   u32x4 wreg[MAXU];
 #pragma unroll
   for (int k = 0; k < MAXU; ++k) {
-    const int u = tid + 256 * k;
+    const int u = tid + NT * k;
     wreg[k] = u32x4{0u, 0u, 0u, 0u};
     if (u < rows * units) {
       const int row = u / units, c8 = (u % units) * 8;
@@ -757,18 +980,18 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
       }
     }
   }
-  const int64_t mlbase = static_cast<int64_t>(bseq) * S * heads + h;
+  const int64_t mlbase = static_cast<int64_t>(wseq) * S * heads + h;
   float2 mlv[MAXSL];
 #pragma unroll
   for (int k = 0; k < MAXSL; ++k) {
     const int s = sl + 16 * k;
-    mlv[k] = (s < S) ? *reinterpret_cast<const float2 *>(ml + 2 * (mlbase + static_cast<int64_t>(s) * heads))
-                     : float2{-INFINITY, 0.f};
+    mlv[k] = (tid < 256 && s < S) ? *reinterpret_cast<const float2 *>(ml + 2 * (mlbase + static_cast<int64_t>(s) * heads))
+                                  : float2{-INFINITY, 0.f};
   }
   // partial rows of (sequence, split, head): wavefront-blocked layout
   // [sequence][split][r / RW][head][RW]; consecutive splits are heads * r apart
   const int jrow = j0 + min(jj0, rows - 8);
-  const uint16_t *psrc = opart + (static_cast<int64_t>(bseq) * S * (r / RW) + jrow / RW) * heads * RW +
+  const uint16_t *psrc = opart + (static_cast<int64_t>(pseq) * S * (r / RW) + jrow / RW) * heads * RW +
                          static_cast<int64_t>(h) * RW + jrow % RW;
   const int64_t sstride = static_cast<int64_t>(heads) * r;
   u32x4 pv[kMergeBatch];
@@ -778,8 +1001,9 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
     if (rvalid && k < S) pv[k] = *reinterpret_cast<const u32x4 *>(psrc + k * sstride);
   }
 
-  // ---- split weights: w_s = 2^(m_s - M) l_s / sum
-  {
+  // ---- split weights: w_s = 2^(m_s - M) l_s / sum (threads 0..255; the
+  // 16 lanes of a sequence are one DPP row)
+  if (tid < 256) {
     float mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < MAXSL; ++k) mx = fmaxf(mx, mlv[k].x);
@@ -791,24 +1015,24 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
     for (int k = 0; k < MAXSL; ++k) {
       const int s = sl + 16 * k;
       const float w = (mx == -INFINITY || s >= S) ? 0.f : __builtin_amdgcn_exp2f(mlv[k].x - mx) * mlv[k].y;
-      if (s < S) wts[bi * S + s] = w;
+      if (s < S) wts[wbi * S + s] = w;
       den += w;
     }
     for (int s = sl + 16 * MAXSL; s < S; s += 16) {
       const int64_t o = mlbase + static_cast<int64_t>(s) * heads;
       const float w = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[2 * o] - mx) * ml[2 * o + 1];
-      wts[bi * S + s] = w;
+      wts[wbi * S + s] = w;
       den += w;
     }
     den = dpp_reduce<16, false>(den);
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int s = sl; s < S; s += 16) wts[bi * S + s] *= inv;
+    for (int s = sl; s < S; s += 16) wts[wbi * S + s] *= inv;
   }
 
   // ---- W registers -> LDS (bf16)
 #pragma unroll
   for (int k = 0; k < MAXU; ++k) {
-    const int u = tid + 256 * k;
+    const int u = tid + NT * k;
     if (u < rows * units) {
       const int row = u / units, c8 = (u % units) * 8;
       u32x4 v = wreg[k];
@@ -827,11 +1051,11 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
   __syncthreads();
 
   // ---- merged O~ rows
-  {
+  if (pbi < BB) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const float w = (k < S) ? wts[bi * S + k] : 0.f;
+      const float w = (k < S) ? wts[min(pbi, nbb - 1) * S + k] : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[2 * e] = fmaf(w, __uint_as_float(pv[k][e] << 16), acc[2 * e]);
@@ -846,7 +1070,7 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
       }
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
-        const float w = (s0 + k < S) ? wts[bi * S + s0 + k] : 0.f;
+        const float w = (s0 + k < S) ? wts[min(pbi, nbb - 1) * S + s0 + k] : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc[2 * e] = fmaf(w, __uint_as_float(pv[k][e] << 16), acc[2 * e]);
@@ -859,16 +1083,16 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(const uint16_t *__restr
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     }
     // A operand of K block jj0 / 32: lane 16 ((jj0 / 8) % 4) + sequence
-    aop[(jj0 >> 5) * 64 + 16 * ((jj0 >> 3) & 3) + bi] =
+    aop[(jj0 >> 5) * 64 + 16 * ((jj0 >> 3) & 3) + pbi] =
         u32x4{cvt_bf16x2(acc[0], acc[1]), cvt_bf16x2(acc[2], acc[3]),
               cvt_bf16x2(acc[4], acc[5]), cvt_bf16x2(acc[6], acc[7])};
   }
   __syncthreads();
 
-  // ---- O~ W^u_v,h: wavefront w takes 16-column blocks w, w + 4, ...
+  // ---- O~ W^u_v,h: wavefront w takes 16-column blocks w, w + 8, ...
   const int li = lane & 15, lg = lane >> 4;
   const int nkb = rows / 32;
-  for (int nb = wave; nb < d / 16; nb += 4) {
+  for (int nb = wave; nb < d / 16; nb += NT / 64) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const uint8_t *trb = wl + (8 * lg + (li >> 2)) * WRS + (nb * 16 + 4 * (li & 3)) * 2;
     for (int kb = 0; kb < nkb; ++kb) {
@@ -1049,7 +1273,7 @@ int kpl_of(int c_dtype) { return c_dtype == QSVD_I4 ? 4 : (c_dtype == QSVD_I8 ? 
 template <int CT, int NHB, int NKB, int T, int D>
 hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
   auto kern = stream_mfma_kernel<CT, NHB, NKB, T, D>;
-  const size_t lds = stream_lds_bytes(W, NHB, NKB, T);
+  const size_t lds = stream_lds_bytes(W, NHB, NKB, T, CT == CT_BF16 ? 0 : (CT == CT_I4 ? 1 : 2));
   hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(sp.ntasks), dim3(W * 64), lds, s>>>(sp);
@@ -1059,7 +1283,13 @@ hipError_t launch_stream_t(const StreamParams &sp, int W, hipStream_t s) {
 template <int CT, int NHB, int NKB>
 hipError_t launch_stream_tile(const StreamParams &sp, const MfmaShape &sh, hipStream_t s) {
   if constexpr (CT != CT_BF16 && NKB <= 8) {
-    if (sh.T == 64) return launch_stream_t<CT, NHB, NKB, 64, 1>(sp, sh.W, s);
+    if (sh.T == 64) {
+      if constexpr (stream_depth_fits(CT == CT_I4, NHB, NKB, 3))
+        if (sh.D == 3) return launch_stream_t<CT, NHB, NKB, 64, 3>(sp, sh.W, s);
+      if constexpr (stream_depth_fits(CT == CT_I4, NHB, NKB, 2))
+        if (sh.D >= 2) return launch_stream_t<CT, NHB, NKB, 64, 2>(sp, sh.W, s);
+      return launch_stream_t<CT, NHB, NKB, 64, 1>(sp, sh.W, s);
+    }
   }
   if constexpr (NHB == 2) {
     return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);  // mfma_shape pairs NHB = 2 with T >= 32
@@ -1154,23 +1384,35 @@ hipError_t launch_merge_f32(const DecodeArgs &a, const DecodePlan &p, const floa
   return hipGetLastError();
 }
 
-size_t merge_mfma_lds(int d, int S) {
-  return static_cast<size_t>(kMergeRows) * (d * 2 + 16) + (kMergeRows / 32) * 64 * 16 +
+size_t merge_mfma_lds(int MR, int d, int S) {
+  return static_cast<size_t>(MR) * (d * 2 + 16) + static_cast<size_t>(MR / 32) * 64 * 16 +
          static_cast<size_t>(16) * S * sizeof(float);
+}
+
+template <typename WT, int MR>
+hipError_t launch_merge_mfma_t(const DecodeArgs &a, const DecodePlan &p, const uint16_t *opart,
+                               const float *ml, float *opj, hipStream_t s) {
+  const size_t lds = merge_mfma_lds(MR, a.d, p.splits);
+  auto kern = merge_mfma_kernel<WT, MR>;
+  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
+  if (e != hipSuccess) return e;
+  kern<<<dim3(p.jc, a.heads, (a.b + 15) / 16), dim3(kMergeThreads), lds, s>>>(
+      opart, ml, static_cast<const WT *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
+      p.splits, p.rw);
+  return hipGetLastError();
 }
 
 template <typename WT>
 hipError_t launch_merge_mfma(const DecodeArgs &a, const DecodePlan &p, const uint16_t *opart,
                              const float *ml, float *opj, hipStream_t s) {
-  const int JC = (a.r + kMergeRows - 1) / kMergeRows;
-  const size_t lds = merge_mfma_lds(a.d, p.splits);
-  auto kern = merge_mfma_kernel<WT>;
-  hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
-  if (e != hipSuccess) return e;
-  kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
-      opart, ml, static_cast<const WT *>(a.Wu_v), a.wu_scale_v, opj, a.b, a.r, a.heads, a.d,
-      p.splits, p.rw);
-  return hipGetLastError();
+  switch (p.merge_rows) {
+    case 32: return launch_merge_mfma_t<WT, 32>(a, p, opart, ml, opj, s);
+    case 64: return launch_merge_mfma_t<WT, 64>(a, p, opart, ml, opj, s);
+    case 96: return launch_merge_mfma_t<WT, 96>(a, p, opart, ml, opj, s);
+    case 128: return launch_merge_mfma_t<WT, 128>(a, p, opart, ml, opj, s);
+    case 192: return launch_merge_mfma_t<WT, 192>(a, p, opart, ml, opj, s);
+    default: return launch_merge_mfma_t<WT, 256>(a, p, opart, ml, opj, s);
+  }
 }
 
 template <typename WT, int DK>
@@ -1208,11 +1450,12 @@ bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
     MfmaShape s{};
     s.W = W;
     s.NKB = nkb;
-    s.NHB = (heads > 16 && nkb <= 6 && stream_lds_bytes(W, 2, nkb, 32) <= kMaxLds) ? 2 : 1;
-    s.T = (nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32) <= kMaxLds) ? 32 : 16;
+    const int kind = c_dtype == QSVD_BF16 ? 0 : (c_dtype == QSVD_I4 ? 1 : 2);
+    s.NHB = (heads > 16 && nkb <= 6 && stream_lds_bytes(W, 2, nkb, 32, kind) <= kMaxLds) ? 2 : 1;
+    s.T = (nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32, kind) <= kMaxLds) ? 32 : 16;
     // quantised codes stage in few registers: a 64-token tile halves the
     // per-token share of the barriers and the softmax where LDS holds it
-    if (c_dtype != QSVD_BF16 && s.T == 32 && nkb <= 8 && stream_lds_bytes(W, s.NHB, nkb, 64) <= kMaxLds)
+    if (c_dtype != QSVD_BF16 && s.T == 32 && nkb <= 8 && stream_lds_bytes(W, s.NHB, nkb, 64, kind) <= kMaxLds)
       s.T = 64;
     // tuning override of the tile (32: one tile of loads in flight, 16: two)
     static const int tile_env = [] {
@@ -1220,8 +1463,18 @@ bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
       return e ? std::atoi(e) : 0;
     }();
     if (tile_env == 16 && s.NHB == 1) s.T = 16;
-    if (tile_env == 32 && nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32) <= kMaxLds) s.T = 32;
-    if (stream_lds_bytes(W, s.NHB, nkb, s.T) > kMaxLds) return false;
+    if (tile_env == 32 && nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32, kind) <= kMaxLds) s.T = 32;
+    // quantised 64-token tiles stage in few registers: two tiles of loads in
+    // flight (tuning override QSVD_STREAM_DEPTH = 1..3)
+    s.D = (s.T == 16) ? 2 : 1;
+    if (s.T == 64 && stream_depth_fits(kind == 1, s.NHB, nkb, 2)) s.D = 2;
+    static const int depth_env = [] {
+      const char *e = std::getenv("QSVD_STREAM_DEPTH");
+      return e ? std::atoi(e) : 0;
+    }();
+    if (s.T == 64 && depth_env >= 1 && depth_env <= 3 && stream_depth_fits(kind == 1, s.NHB, nkb, depth_env))
+      s.D = depth_env;
+    if (stream_lds_bytes(W, s.NHB, nkb, s.T, kind) > kMaxLds) return false;
     if (out) *out = s;
     return true;
   }
@@ -1275,12 +1528,30 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
     }
     p.splits = static_cast<int>((L + p.chunk - 1) / p.chunk);
   }
+  // merge chunk: the fewest rounds of workgroups over the compute units, then
+  // the most workgroups (smallest chunk) within that many rounds
+  if (p.mfma) {
+    const int64_t groups = static_cast<int64_t>(heads) * ((b + 15) / 16);
+    int best = 256;
+    int64_t best_rounds = INT64_MAX;
+    for (int mr : {256, 192, 128, 96, 64, 32}) {
+      const int64_t jc = (r + mr - 1) / mr;
+      const int64_t rounds = (jc * groups + kNumCU - 1) / kNumCU;
+      if (rounds <= best_rounds) {
+        best_rounds = rounds;
+        best = mr;
+      }
+    }
+    p.merge_rows = best;
+  } else {
+    p.merge_rows = kMergeRows;
+  }
+  p.jc = (r + p.merge_rows - 1) / p.merge_rows;
   const size_t esz = p.mfma ? 2 : 4;
   p.qt_bytes = align256(static_cast<size_t>(b) * heads * r * esz);
   const size_t opart = align256(static_cast<size_t>(b) * p.splits * heads * r * esz);
   const size_t ml = align256(static_cast<size_t>(b) * p.splits * heads * 2 * sizeof(float));
-  const int JC = (r + kMergeRows - 1) / kMergeRows;
-  const size_t opj = align256(static_cast<size_t>(JC) * b * heads * d * sizeof(float));
+  const size_t opj = align256(static_cast<size_t>(p.jc) * b * heads * d * sizeof(float));
   p.part_bytes = opart + ml + opj;
   if (p.wide) p.part_bytes += align256(p.wp.s_bytes) + align256(p.wp.m1_bytes);
   p.total = p.qt_bytes + p.part_bytes;
@@ -1314,7 +1585,7 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
   // ---- stream (two passes for wide latents with many heads)
   if (p.wide) {
     uint8_t *wbase = reinterpret_cast<uint8_t *>(opj) +
-                     align256(static_cast<size_t>((a.r + kMergeRows - 1) / kMergeRows) * a.b * a.heads * a.d * sizeof(float));
+                     align256(static_cast<size_t>(p.jc) * a.b * a.heads * a.d * sizeof(float));
     WideArgs wa{};
     wa.C = a.C;
     wa.qt = static_cast<const uint16_t *>(qt);
@@ -1389,7 +1660,7 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
   {
     LaunchTimer t("decode_finalize", s);
     const int64_t n = static_cast<int64_t>(a.b) * a.heads * a.d;
-    const int JC = (a.r + kMergeRows - 1) / kMergeRows;
+    const int JC = p.jc;
     const dim3 grid(static_cast<unsigned>((n / 4 + 255) / 256)), block(256);
     if (a.o_dtype == QSVD_BF16)
       finalize_kernel<uint16_t><<<grid, block, 0, s>>>(opj, static_cast<uint16_t *>(a.O), n, JC);

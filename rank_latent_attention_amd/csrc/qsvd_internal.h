@@ -11,18 +11,14 @@
 namespace qsvd {
 
 // ---------------------------------------------------------------- timing
-// RAII bracket around one kernel launch: records a HIP event pair on the
-// launch stream when a timing session is active on this thread.
+// Marks a kernel launch for the timing session of this thread: when a session
+// is active, the constructor records the launch-boundary event on the launch
+// stream (the launch follows it; see qsvd_timing_begin).
 class LaunchTimer {
  public:
   LaunchTimer(const char *name, hipStream_t stream);
-  ~LaunchTimer();
   LaunchTimer(const LaunchTimer &) = delete;
   LaunchTimer &operator=(const LaunchTimer &) = delete;
-
- private:
-  int slot_;
-  hipStream_t stream_;
 };
 
 // Allow `kernel` (a __global__ function's address) `bytes` of dynamic LDS on
@@ -143,7 +139,7 @@ hipError_t launch_wide_values(const WideArgs &a, hipStream_t s);
 // Shape of the MFMA stream kernel: W wavefronts of RW = 32 NKB latent columns
 // each (r = W RW), NHB 16-head blocks per workgroup, T tokens per tile.
 struct MfmaShape {
-  int W, NKB, NHB, T;
+  int W, NKB, NHB, T, D;   // D: token tiles of loads in flight (quantised 64-token tiles)
 };
 
 // True when the MFMA stream kernel supports latent width r for the cache
@@ -161,6 +157,8 @@ struct DecodePlan {
   bool wide;         // two-pass decode (score pass + value pass) instead of the stream kernel
   WidePlanInfo wp;   // its chunking (wide only)
   int rw;            // columns per partial block of the split partials
+  int merge_rows;    // latent rows per merge workgroup (MFMA paths)
+  int jc;            // merge chunks along r (chunk shares summed by the finalize)
   size_t qt_bytes;   // absorbed queries
   size_t part_bytes; // per-split partial state
   size_t total;
