@@ -187,6 +187,30 @@ qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *
                                void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * qsvd_decode_attn_noalloc: qsvd_decode_attn without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc).  The call
+ * allocates nothing: its scratch is a library-owned device array of 64 MiB
+ * (one per GPU the library runs on, held until the process ends) that the
+ * library locates with hipGetSymbolAddress once per device.  Arguments and
+ * results are those of qsvd_decode_attn with the same kernels.
+ *   Errors: as qsvd_decode_attn; QSVD_ERR_WORKSPACE when the shape needs more
+ *   than 64 MiB of scratch (qsvd_decode_workspace_bytes tells how much; the
+ *   7B, 13B and W8A4 decode shapes need at most about 40 MiB).
+ *   Every call on one GPU uses that GPU's single scratch array: calls that
+ *   overlap in time on one GPU (other streams, other threads) race and must
+ *   be ordered by the caller.  Nothing in the array needs clearing between
+ *   calls (each call writes every scratch value before reading it).
+ */
+qsvd_status_t qsvd_decode_attn_noalloc(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                       qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
+                                       const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
+                                       const float *wu_scale_k, const float *wu_scale_v, int32_t b,
+                                       int64_t L, int32_t r, int32_t heads, int32_t d,
+                                       float softmax_scale, int32_t splits, void *O,
+                                       qsvd_dtype_t o_dtype, void *hip_stream);
+
+/*
  * qsvd_decode_attn_explicit: the same decode step with each head's keys and
  * values rebuilt explicitly on chip, K_h = C W^u_k,h and V_h = C W^u_v,h,
  * tile by tile (never written to memory), optionally with rotary position

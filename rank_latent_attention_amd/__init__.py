@@ -16,6 +16,7 @@ __all__ = [
     "F32", "BF16", "I8", "I4", "QsvdError", "lib", "library_path",
     "qsvd_quantize_latent", "qsvd_project", "qsvd_pack_weight",
     "qsvd_decode_workspace_bytes", "qsvd_decode_default_splits", "qsvd_decode_attn",
+    "qsvd_decode_attn_noalloc",
     "qsvd_decode_explicit_workspace_bytes", "qsvd_decode_attn_explicit",
     "qsvd_decode_headwise_workspace_bytes", "qsvd_decode_attn_headwise",
     "qsvd_status_string", "qsvd_last_error", "timing", "EXPORTED",
@@ -28,7 +29,8 @@ library_path = os.path.join(_PKG, "libqsvd.so")
 # every symbol include/qsvd.h declares
 EXPORTED = (
     "qsvd_quantize_latent", "qsvd_project", "qsvd_pack_weight", "qsvd_decode_workspace_bytes",
-    "qsvd_decode_attn", "qsvd_decode_default_splits", "qsvd_decode_explicit_workspace_bytes",
+    "qsvd_decode_attn", "qsvd_decode_attn_noalloc", "qsvd_decode_default_splits",
+    "qsvd_decode_explicit_workspace_bytes",
     "qsvd_decode_attn_explicit", "qsvd_decode_headwise_workspace_bytes",
     "qsvd_decode_attn_headwise", "qsvd_status_string", "qsvd_last_error",
     "qsvd_timing_begin", "qsvd_timing_end",
@@ -67,6 +69,8 @@ def lib() -> ctypes.CDLL:
     L.qsvd_decode_default_splits.argtypes = [i32, i64, i32, i32, i32, i32]
     L.qsvd_decode_attn.argtypes = [vp, i32, vp, i32, f32p, i32, vp, vp, i32, f32p, f32p, i32, i64,
                                    i32, i32, i32, ctypes.c_float, i32, vp, i32, vp, sz, vp]
+    L.qsvd_decode_attn_noalloc.argtypes = [vp, i32, vp, i32, f32p, i32, vp, vp, i32, f32p, f32p, i32,
+                                           i64, i32, i32, i32, ctypes.c_float, i32, vp, i32, vp]
     L.qsvd_decode_explicit_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
     L.qsvd_decode_explicit_workspace_bytes.restype = sz
     L.qsvd_decode_attn_explicit.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
@@ -82,6 +86,7 @@ def lib() -> ctypes.CDLL:
     L.qsvd_timing_begin.argtypes = [i32]
     L.qsvd_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
     for name in ("qsvd_quantize_latent", "qsvd_project", "qsvd_pack_weight", "qsvd_decode_attn",
+                 "qsvd_decode_attn_noalloc",
                  "qsvd_decode_attn_explicit", "qsvd_decode_attn_headwise", "qsvd_timing_begin", "qsvd_timing_end", "qsvd_decode_default_splits"):
         getattr(L, name).restype = i32
     _lib = L
@@ -152,6 +157,16 @@ def qsvd_decode_attn(q, q_dtype, C, c_dtype, c_scales, c_group, Wu_k, Wu_v, wu_d
                                   _ptr(O), o_dtype, _ptr(workspace), workspace_bytes,
                                   _stream(stream)),
            "qsvd_decode_attn")
+
+
+def qsvd_decode_attn_noalloc(q, q_dtype, C, c_dtype, c_scales, c_group, Wu_k, Wu_v, wu_dtype,
+                             wu_scale_k, wu_scale_v, b, L, r, heads, d, softmax_scale, splits, O,
+                             o_dtype, stream=None):
+    _check(lib().qsvd_decode_attn_noalloc(_ptr(q), q_dtype, _ptr(C), c_dtype, _ptr(c_scales), c_group,
+                                          _ptr(Wu_k), _ptr(Wu_v), wu_dtype, _ptr(wu_scale_k),
+                                          _ptr(wu_scale_v), b, L, r, heads, d, float(softmax_scale),
+                                          splits, _ptr(O), o_dtype, _stream(stream)),
+           "qsvd_decode_attn_noalloc")
 
 
 def qsvd_decode_explicit_workspace_bytes(b, L, r, heads, d) -> int:

@@ -101,6 +101,16 @@ hipError_t set_dynamic_lds(const void *kernel, size_t bytes) {
   return hipSuccess;
 }
 
+qsvd_status_t report(qsvd_status_t s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
 }  // namespace qsvd
 
 extern "C" {
@@ -389,22 +399,6 @@ qsvd_status_t qsvd_decode_attn_headwise(const void *q, qsvd_dtype_t q_dtype, con
                        "decode_attn_headwise");
 }
 
-namespace qsvd {
-
-// Validation and launch of one decode step (qsvd_decode_attn); workspace ==
-// nullptr with workspace_bytes == 0 only asks for the plan's size through
-// *need without launching (the arguments are still validated).
-qsvd_status_t decode_attn_checked(const void *q, qsvd_dtype_t q_dtype, const void *C,
-                                  qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
-                                  const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
-                                  const float *wu_scale_k, const float *wu_scale_v, int32_t b,
-                                  int64_t L, int32_t r, int32_t heads, int32_t d,
-                                  float softmax_scale, int32_t splits, void *O, qsvd_dtype_t o_dtype,
-                                  void *workspace, size_t workspace_bytes, void *hip_stream,
-                                  size_t *need);
-
-}  // namespace qsvd
-
 qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *C,
                                qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
                                const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
@@ -417,82 +411,6 @@ qsvd_status_t qsvd_decode_attn(const void *q, qsvd_dtype_t q_dtype, const void *
                                    O, o_dtype, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
-qsvd_status_t qsvd::decode_attn_checked(const void *q, qsvd_dtype_t q_dtype, const void *C,
-                                        qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
-                                        const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
-                                        const float *wu_scale_k, const float *wu_scale_v, int32_t b,
-                                        int64_t L, int32_t r, int32_t heads, int32_t d,
-                                        float softmax_scale, int32_t splits, void *O,
-                                        qsvd_dtype_t o_dtype, void *workspace, size_t workspace_bytes,
-                                        void *hip_stream, size_t *need) {
-  qsvd_status_t st = validate_decode_shape(b, L, r, heads, d, c_dtype, splits);
-  if (st != QSVD_OK) return st;
-  if (c_dtype == QSVD_F32) {
-    if (q_dtype != QSVD_F32 || wu_dtype != QSVD_F32 || o_dtype != QSVD_F32)
-      return fail(QSVD_ERR_UNSUPPORTED, "decode: F32 cache needs F32 q, W^u and O");
-  } else {
-    if (q_dtype != QSVD_BF16)
-      return fail(QSVD_ERR_UNSUPPORTED, "decode: %s cache needs BF16 q", dtype_name(c_dtype));
-    if (wu_dtype != QSVD_BF16 && wu_dtype != QSVD_I8)
-      return fail(QSVD_ERR_UNSUPPORTED, "decode: W^u dtype %s (BF16 or I8)", dtype_name(wu_dtype));
-    if (o_dtype != QSVD_BF16 && o_dtype != QSVD_F32)
-      return fail(QSVD_ERR_INVALID, "decode: o_dtype %s", dtype_name(o_dtype));
-  }
-  if (c_dtype == QSVD_I4) {
-    if (c_group != 128) return fail(QSVD_ERR_UNSUPPORTED, "decode: int4 cache needs c_group 128");
-    if (!c_scales) return fail(QSVD_ERR_INVALID, "decode: int4 cache needs c_scales");
-  } else if (c_dtype == QSVD_I8) {
-    if (c_group != 0) return fail(QSVD_ERR_UNSUPPORTED, "decode: int8 cache is per token (c_group 0)");
-    if (!c_scales) return fail(QSVD_ERR_INVALID, "decode: int8 cache needs c_scales");
-  } else {
-    if (c_scales || c_group != 0)
-      return fail(QSVD_ERR_INVALID, "decode: %s cache takes no scales", dtype_name(c_dtype));
-  }
-  if (wu_dtype == QSVD_I8) {
-    if (!wu_scale_k || !wu_scale_v)
-      return fail(QSVD_ERR_INVALID, "decode: int8 W^u needs wu_scale_k and wu_scale_v");
-  } else if (wu_scale_k || wu_scale_v) {
-    return fail(QSVD_ERR_INVALID, "decode: %s W^u takes no scales", dtype_name(wu_dtype));
-  }
-  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
-    return fail(QSVD_ERR_INVALID, "decode: softmax_scale must be positive and finite");
-  if (!q || !C || !Wu_k || !Wu_v || !O) return fail(QSVD_ERR_INVALID, "decode: NULL pointer");
-  if (!aligned16(q) || !aligned16(C) || !aligned16(Wu_k) || !aligned16(Wu_v) || !aligned16(O) ||
-      (c_scales && !aligned4(c_scales)) || (workspace && !aligned16(workspace)))
-    return fail(QSVD_ERR_INVALID, "decode: misaligned pointer");
-  const qsvd::DecodePlan plan = qsvd::plan_decode(b, L, r, heads, d, c_dtype, splits);
-  if (need) {
-    *need = plan.total;
-    if (!workspace && workspace_bytes == 0) return ok();
-  }
-  if (!workspace || workspace_bytes < plan.total)
-    return fail(QSVD_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
-                plan.total);
-  qsvd::DecodeArgs a{};
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.C = C;
-  a.c_dtype = c_dtype;
-  a.c_scales = c_scales;
-  a.c_group = c_group;
-  a.Wu_k = Wu_k;
-  a.Wu_v = Wu_v;
-  a.wu_dtype = wu_dtype;
-  a.wu_scale_k = wu_scale_k;
-  a.wu_scale_v = wu_scale_v;
-  a.b = b;
-  a.L = L;
-  a.r = r;
-  a.heads = heads;
-  a.d = d;
-  a.softmax_scale = softmax_scale;
-  a.splits = splits;
-  a.O = O;
-  a.o_dtype = o_dtype;
-  a.workspace = workspace;
-  return device_status(qsvd::launch_decode(a, plan, static_cast<hipStream_t>(hip_stream)),
-                       "decode_attn");
-}
 
 qsvd_status_t qsvd_timing_begin(int32_t max_launches) {
   TimingSession &t = g_timing;
@@ -565,3 +483,84 @@ qsvd_status_t qsvd_timing_end(qsvd_kernel_time_t *out, int32_t max_out, int32_t 
 }
 
 }  // extern "C"
+
+namespace qsvd {
+
+qsvd_status_t decode_attn_checked(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                  qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
+                                  const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
+                                  const float *wu_scale_k, const float *wu_scale_v, int32_t b,
+                                  int64_t L, int32_t r, int32_t heads, int32_t d,
+                                  float softmax_scale, int32_t splits, void *O, qsvd_dtype_t o_dtype,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream,
+                                  size_t *need) {
+  qsvd_status_t st = validate_decode_shape(b, L, r, heads, d, c_dtype, splits);
+  if (st != QSVD_OK) return st;
+  if (c_dtype == QSVD_F32) {
+    if (q_dtype != QSVD_F32 || wu_dtype != QSVD_F32 || o_dtype != QSVD_F32)
+      return fail(QSVD_ERR_UNSUPPORTED, "decode: F32 cache needs F32 q, W^u and O");
+  } else {
+    if (q_dtype != QSVD_BF16)
+      return fail(QSVD_ERR_UNSUPPORTED, "decode: %s cache needs BF16 q", dtype_name(c_dtype));
+    if (wu_dtype != QSVD_BF16 && wu_dtype != QSVD_I8)
+      return fail(QSVD_ERR_UNSUPPORTED, "decode: W^u dtype %s (BF16 or I8)", dtype_name(wu_dtype));
+    if (o_dtype != QSVD_BF16 && o_dtype != QSVD_F32)
+      return fail(QSVD_ERR_INVALID, "decode: o_dtype %s", dtype_name(o_dtype));
+  }
+  if (c_dtype == QSVD_I4) {
+    if (c_group != 128) return fail(QSVD_ERR_UNSUPPORTED, "decode: int4 cache needs c_group 128");
+    if (!c_scales) return fail(QSVD_ERR_INVALID, "decode: int4 cache needs c_scales");
+  } else if (c_dtype == QSVD_I8) {
+    if (c_group != 0) return fail(QSVD_ERR_UNSUPPORTED, "decode: int8 cache is per token (c_group 0)");
+    if (!c_scales) return fail(QSVD_ERR_INVALID, "decode: int8 cache needs c_scales");
+  } else {
+    if (c_scales || c_group != 0)
+      return fail(QSVD_ERR_INVALID, "decode: %s cache takes no scales", dtype_name(c_dtype));
+  }
+  if (wu_dtype == QSVD_I8) {
+    if (!wu_scale_k || !wu_scale_v)
+      return fail(QSVD_ERR_INVALID, "decode: int8 W^u needs wu_scale_k and wu_scale_v");
+  } else if (wu_scale_k || wu_scale_v) {
+    return fail(QSVD_ERR_INVALID, "decode: %s W^u takes no scales", dtype_name(wu_dtype));
+  }
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
+    return fail(QSVD_ERR_INVALID, "decode: softmax_scale must be positive and finite");
+  if (!q || !C || !Wu_k || !Wu_v || !O) return fail(QSVD_ERR_INVALID, "decode: NULL pointer");
+  if (!aligned16(q) || !aligned16(C) || !aligned16(Wu_k) || !aligned16(Wu_v) || !aligned16(O) ||
+      (c_scales && !aligned4(c_scales)) || (workspace && !aligned16(workspace)))
+    return fail(QSVD_ERR_INVALID, "decode: misaligned pointer");
+  const DecodePlan plan = plan_decode(b, L, r, heads, d, c_dtype, splits);
+  if (need) {
+    *need = plan.total;
+    if (!workspace && workspace_bytes == 0) return ok();
+  }
+  if (!workspace || workspace_bytes < plan.total)
+    return fail(QSVD_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
+                plan.total);
+  DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.C = C;
+  a.c_dtype = c_dtype;
+  a.c_scales = c_scales;
+  a.c_group = c_group;
+  a.Wu_k = Wu_k;
+  a.Wu_v = Wu_v;
+  a.wu_dtype = wu_dtype;
+  a.wu_scale_k = wu_scale_k;
+  a.wu_scale_v = wu_scale_v;
+  a.b = b;
+  a.L = L;
+  a.r = r;
+  a.heads = heads;
+  a.d = d;
+  a.softmax_scale = softmax_scale;
+  a.splits = splits;
+  a.O = O;
+  a.o_dtype = o_dtype;
+  a.workspace = workspace;
+  return device_status(launch_decode(a, plan, static_cast<hipStream_t>(hip_stream)),
+                       "decode_attn");
+}
+
+}  // namespace qsvd

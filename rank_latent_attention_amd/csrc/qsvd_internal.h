@@ -168,4 +168,19 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
 
 hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s);
 
+// Argument validation and launch of one qsvd_decode_attn step.  With need
+// non-NULL it receives the workspace size of the plan; workspace == NULL with
+// workspace_bytes == 0 then validates and sizes without launching.
+qsvd_status_t decode_attn_checked(const void *q, qsvd_dtype_t q_dtype, const void *C,
+                                  qsvd_dtype_t c_dtype, const float *c_scales, int32_t c_group,
+                                  const void *Wu_k, const void *Wu_v, qsvd_dtype_t wu_dtype,
+                                  const float *wu_scale_k, const float *wu_scale_v, int32_t b,
+                                  int64_t L, int32_t r, int32_t heads, int32_t d,
+                                  float softmax_scale, int32_t splits, void *O, qsvd_dtype_t o_dtype,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream,
+                                  size_t *need);
+
+// Record a failure message for qsvd_last_error and return s.
+qsvd_status_t report(qsvd_status_t s, const char *fmt, ...);
+
 }  // namespace qsvd
