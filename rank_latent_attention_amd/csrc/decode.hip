@@ -480,8 +480,13 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   const uint32_t voff0 = static_cast<uint32_t>(li * row_bytes + Tr::byte_offset(j0w + EPL * lg));
   u32x4 stage[D][NTB][NLD];
   float sscale[D][NTB][NLD];
-  auto load_rows = [&](auto BUF, int64_t t0, int tb) {
+  // Branch-free: a tile past the split's last one (valid == false) is loaded
+  // through an empty resource, which returns zeros without touching memory,
+  // so the code path (and the compiler's waits for the loads) is the same
+  // for every tile.
+  auto load_rows = [&](auto BUF, int64_t t0_in, int tb, bool valid) {
     constexpr int bf = decltype(BUF)::value;
+    const int64_t t0 = valid ? t0_in : L;
     const int64_t row0 = static_cast<int64_t>(seq) * L + t0;
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(p.C + row0 * row_bytes, (L - t0) * row_bytes);
     const uint32_t vo = voff0 + static_cast<uint32_t>(tb * 16 * row_bytes);
@@ -510,8 +515,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   auto prefetch = [&](auto BUF) {
     constexpr int k = decltype(BUF)::value;
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-      if (ntiles > k) load_rows(BUF, tile_start(k), tb);
+    for (int tb = 0; tb < NTB; ++tb) load_rows(BUF, tile_start(k), tb, ntiles > k);
   };
   prefetch(std::integral_constant<int, 0>{});
   if constexpr (D > 1) prefetch(std::integral_constant<int, 1>{});
@@ -580,7 +584,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
     m_s[i] = -INFINITY;
     l_s[i] = 0.f;
   }
-  __syncthreads();
+  lds_barrier();   // the first tiles' loads stay in flight
 
   auto body = [&](auto BUF, int it) {
     constexpr int bf = decltype(BUF)::value;
@@ -636,7 +640,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         const int jl = 32 * KPL * ld + EPL * lg + 8 * s;
         *reinterpret_cast<u32x4 *>(ct + (tb * 16 + li) * RS + jl * 2) = cv[kb];
       }
-      if (more) load_rows(BUF, next_t0, tb);
+      load_rows(BUF, next_t0, tb, more);
       // partial scores, head-major: lane holds tokens 16 tb + 4 g + (0..3) of head 16 hb + i
       f32x4 part[NHB];
 #pragma unroll
@@ -667,6 +671,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       constexpr int TPI = T / 8;
       for (int item = tid; item < HGP * 8; item += nthreads) {
         const int h = item >> 3, u = item & 7, t0 = u * TPI;
+        const float m_old = m_s[h];
         // rows past W are not read (wave-uniform bound, constant row offsets)
         const float *sph = spart + h * SPR + t0;
         float sc[TPI];
@@ -702,7 +707,6 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
           mx = fmaxf(mx, sc[e]);
         }
         mx = dpp_reduce<8, true>(mx);
-        const float m_old = m_s[h];
         const float m_new = fmaxf(m_old, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
         uint32_t pp[TPI / 2];
@@ -855,7 +859,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
       if (it + 3 < ntiles) body(std::integral_constant<int, 3>{}, it + 3);
     }
   }
-  __syncthreads();
+  lds_barrier();   // every wavefront is done with the C tiles the epilogue reuses
 
   // ---- partial state: O~ / l in bf16, one contiguous block per wavefront
   // ([sequence][split][wavefront][head][RW]), staged in the wavefront's LDS
@@ -1295,6 +1299,7 @@ hipError_t launch_stream_tile(const StreamParams &sp, const MfmaShape &sh, hipSt
     return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);  // mfma_shape pairs NHB = 2 with T >= 32
   } else {
     if (sh.T == 32) return launch_stream_t<CT, NHB, NKB, 32, 1>(sp, sh.W, s);
+    if (sh.D == 1) return launch_stream_t<CT, NHB, NKB, 16, 1>(sp, sh.W, s);
     return launch_stream_t<CT, NHB, NKB, 16, 2>(sp, sh.W, s);
   }
 }
@@ -1474,6 +1479,7 @@ bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
     }();
     if (s.T == 64 && depth_env >= 1 && depth_env <= 3 && stream_depth_fits(kind == 1, s.NHB, nkb, depth_env))
       s.D = depth_env;
+    if (s.T == 16 && depth_env == 1) s.D = 1;
     if (stream_lds_bytes(W, s.NHB, nkb, s.T, kind) > kMaxLds) return false;
     if (out) *out = s;
     return true;
@@ -1506,7 +1512,11 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
     p.rw = r / sh.W;
     // many heads over a wide latent: two passes that each read the cache once
     // beat a single pass whose head groups read it three or more times
-    if (wide_applies(r, heads, c_dtype, G)) {
+    static const bool no_wide = [] {
+      const char *e = std::getenv("QSVD_NO_WIDE");   // tuning override: single pass only
+      return e && std::atoi(e) == 1;
+    }();
+    if (!no_wide && wide_applies(r, heads, c_dtype, G)) {
       p.wide = true;
       wide_plan(b, L, r, heads, &p.wp);
       p.splits = p.wp.splits;
