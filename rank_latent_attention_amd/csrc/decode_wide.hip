@@ -100,17 +100,17 @@ __global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
   // j0w + 32 kb + 8 lg .. +8; a block's rows of the next tile are requested
   // as soon as its products have read them
   u32x4 stage[2][NKB];
-  auto load_rows = [&](int it, int tb) {
-    const int64_t t0 = t_begin + static_cast<int64_t>(it) * kWideT;
+  // (branch-free: past the chunk's last tile the resource is empty, which
+  // reads zeros without memory traffic and keeps the compiler's waits exact)
+  auto load_rows = [&](int it, int tb, bool valid) {
+    const int64_t t0 = valid ? t_begin + static_cast<int64_t>(it) * kWideT : t_end;
     const __amdgpu_buffer_rsrc_t rc = wide_rsrc(C + (seq * L + t0) * row_bytes, (t_end - t0) * row_bytes);
     const uint32_t vo = static_cast<uint32_t>((16 * tb + li) * row_bytes + (j0w + 8 * lg) * 2);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) stage[tb][kb] = __builtin_amdgcn_raw_buffer_load_b128(rc, vo + 64 * kb, 0, 0);
   };
-  if (ntiles > 0) {
-    load_rows(0, 0);
-    load_rows(0, 1);
-  }
+  load_rows(0, 0, ntiles > 0);
+  load_rows(0, 1, ntiles > 0);
 
   // absorbed queries as the B operand: head 16 hb + li, columns j0w + 32 kb + 8 lg .. +8
   bf16x8 qf[NH][NKB];
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(512) void wide_scores_kernel(WideArgs p) {
         for (int hb = 0; hb < NH; ++hb)
           sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, stage[tb][kb]),
                                                              qf[hb][kb], sacc[hb], 0, 0, 0);
-      if (it + 1 < ntiles) load_rows(it + 1, tb);
+      load_rows(it + 1, tb, it + 1 < ntiles);
       // lane holds tokens 16 tb + 4 lg + (0..3) of head 16 hb + li
 #pragma unroll
       for (int hb = 0; hb < NH; ++hb)

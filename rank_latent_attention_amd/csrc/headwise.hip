@@ -215,6 +215,15 @@ void headwise_stream_kernel(HeadwiseParams p) {
       }
   }
 
+  // RoPE table row of the tile about to be processed (one tile ahead)
+  f32x4 rcos = {0.f, 0.f, 0.f, 0.f}, rsin = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (ROPE) {
+    if (ntiles > 0) {
+      const int64_t off0 = tile_t0(0) * (kHd / 2) + 4 * li;
+      rcos = *reinterpret_cast<const f32x4 *>(p.rope_cos + off0);
+      rsin = *reinterpret_cast<const f32x4 *>(p.rope_sin + off0);
+    }
+  }
   float m = -INFINITY, l = 0.f;
   float ov[KBV][8];   // this lane's tokens' value columns 32 v + 8 lg + c, summed over tiles
 #pragma unroll
@@ -232,9 +241,8 @@ void headwise_stream_kernel(HeadwiseParams p) {
     // with the f16 (cos, sin) pair of the offset
     h16x2 ya[4], yb[4];
     if constexpr (ROPE) {
-      const int64_t off = t0 * (kHd / 2) + 4 * li;
-      const f32x4 c0 = *reinterpret_cast<const f32x4 *>(p.rope_cos + off);
-      const f32x4 s0 = *reinterpret_cast<const f32x4 *>(p.rope_sin + off);
+      // table row t0, loaded one tile ahead
+      const f32x4 c0 = rcos, s0 = rsin;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float y0 = fmaf(qr[j], c0[j], qr[j + 4] * s0[j]);
@@ -242,6 +250,13 @@ void headwise_stream_kernel(HeadwiseParams p) {
         ya[j] = __builtin_convertvector(f32x2{y0, y1}, h16x2);
         yb[j] = __builtin_convertvector(f32x2{y1, -y0}, h16x2);
       }
+      // the next tile's row, requested before the tile prefetch below: vector
+      // loads complete in order, so a row requested after the prefetch and used
+      // at the start of the next tile would make that tile wait for the
+      // prefetch as well
+      const int64_t offn = tile_t0(min(it + 1, ntiles - 1)) * (kHd / 2) + 4 * li;
+      rcos = *reinterpret_cast<const f32x4 *>(p.rope_cos + offn);
+      rsin = *reinterpret_cast<const f32x4 *>(p.rope_sin + offn);
     }
     // tile it + NBUF - 1 into the buffer freed by tile it - 1 (past the end: a
     // repeat of the last tile, never used)
