@@ -433,7 +433,10 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   static_assert(NKB % KPL == 0, "wavefront columns must be whole 16-byte loads");
   static_assert(T == 16 || T == 32 || T == 64, "tile");
   static_assert(D >= 1 && D <= 4, "prefetch depth");
-  static_assert(HGP * RW * 2 <= T * RS, "the output rows are staged in the wavefront's C tile");
+  // output staging rows: RW + 8 elements apart, so the 16 heads of one store
+  // instruction fall in different LDS banks
+  constexpr int OSTR = RW + 8;
+  static_assert(HGP * OSTR * 2 <= T * RS, "the output rows are staged in the wavefront's C tile");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,17 +513,26 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   };
   auto tile_start = [&](int it) { return (static_cast<int64_t>(split) + static_cast<int64_t>(it) * p.S) * T; };
 
-  // the first D tiles are requested before anything else (buffer k holds
-  // tiles k, k + D, k + 2 D, ...)
+
+  // The first D tiles are requested at once (buffer k holds tiles k, k + D,
+  // k + 2 D, ...).  Quantised caches request the absorbed queries first:
+  // vector loads complete in order, and queries requested after the tiles
+  // would make the offset sums below wait for the tiles as well.
   auto prefetch = [&](auto BUF) {
     constexpr int k = decltype(BUF)::value;
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) load_rows(BUF, tile_start(k), tb, ntiles > k);
   };
-  prefetch(std::integral_constant<int, 0>{});
-  if constexpr (D > 1) prefetch(std::integral_constant<int, 1>{});
-  if constexpr (D > 2) prefetch(std::integral_constant<int, 2>{});
-  if constexpr (D > 3) prefetch(std::integral_constant<int, 3>{});
+  auto prefetch_all = [&]() {
+    prefetch(std::integral_constant<int, 0>{});
+    if constexpr (D > 1) prefetch(std::integral_constant<int, 1>{});
+    if constexpr (D > 2) prefetch(std::integral_constant<int, 2>{});
+    if constexpr (D > 3) prefetch(std::integral_constant<int, 3>{});
+  };
+  if constexpr (CT == CT_BF16) {
+    prefetch_all();
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // Absorbed queries as the B operand of the score product.  K block
   // kb = KPL * ld + s of lane group g covers columns
@@ -533,14 +545,30 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
     for (int kb = 0; kb < NKB; ++kb) {
       const int h = hb * 16 + li;
       const int ld = kb / KPL, s = kb % KPL;
+      const int j = j0w + 32 * KPL * ld + EPL * lg + 8 * s;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < hg) {
-        const int j = j0w + 32 * KPL * ld + EPL * lg + 8 * s;
-        v = *reinterpret_cast<const u32x4 *>(p.qt + (static_cast<int64_t>(seq) * p.heads + h0 + h) * r + j);
+      if constexpr (CT == CT_BF16) {
+        if (h < hg) v = *reinterpret_cast<const u32x4 *>(p.qt + (static_cast<int64_t>(seq) * p.heads + h0 + h) * r + j);
+      } else {
+        // padded heads (h >= hg) read a real head's row: their scores and
+        // value columns are computed and never written (a branch-free load
+        // keeps the compiler's waits exact before the offset sums)
+        v = *reinterpret_cast<const u32x4 *>(p.qt + (static_cast<int64_t>(seq) * p.heads + h0 + min(h, hg - 1)) * r + j);
       }
-      if constexpr (CT == CT_I4) v = i4_order(v);   // the K order of the int4 code operands
       qf[hb][kb] = __builtin_bit_cast(bf16x8, v);
     }
+  if constexpr (CT != CT_BF16) {
+    prefetch_all();
+    // (nothing that reads the queries may be scheduled above the prefetch)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (CT == CT_I4) {   // the K order of the int4 code operands
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        qf[hb][kb] = __builtin_bit_cast(bf16x8, i4_order(__builtin_bit_cast(u32x4, qf[hb][kb])));
+  }
 
   // Quantised caches: the score and value products run on the exact codes
   // plus a constant offset (136 for int4, 128 for int8) and the scales are
@@ -866,7 +894,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   // tile so that the stores are 16-byte and contiguous; and (m, l)
   const int64_t pbase = (static_cast<int64_t>(seq) * p.S + split) * p.heads + h0;
   {
-    uint16_t *ot = reinterpret_cast<uint16_t *>(ct);  // [HGP][RW]
+    uint16_t *ot = reinterpret_cast<uint16_t *>(ct);  // [HGP][OSTR]
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const int h = hb * 16 + li;
@@ -890,7 +918,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
         }
         if constexpr (CT == CT_I4) {
           // K positions 16 jb + 4 g + e of the int4 order back to columns
-          uint16_t *row = ot + h * RW + jb * 16 + 8 * (lg >> 1);
+          uint16_t *row = ot + h * OSTR + jb * 16 + 8 * (lg >> 1);
           const int p0 = 4 * (lg & 1);
           const uint32_t a = cvt_bf16x2(o[0], o[1]), c = cvt_bf16x2(o[2], o[3]);
           row[i4_column(p0)] = static_cast<uint16_t>(a);
@@ -898,7 +926,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
           row[i4_column(p0 + 2)] = static_cast<uint16_t>(c);
           row[i4_column(p0 + 3)] = static_cast<uint16_t>(c >> 16);
         } else {
-          *reinterpret_cast<u32x2 *>(ot + h * RW + jb * 16 + 4 * lg) =
+          *reinterpret_cast<u32x2 *>(ot + h * OSTR + jb * 16 + 4 * lg) =
               u32x2{cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3])};
         }
       }
@@ -908,7 +936,8 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
     uint16_t *dst = p.opart + ((static_cast<int64_t>(seq) * p.S + split) * W + wave) *
                                   static_cast<int64_t>(p.heads) * RW + static_cast<int64_t>(h0) * RW;
     for (int u = lane; u < hg * RW / 8; u += 64)
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(ot + u * 8), reinterpret_cast<u32x4 *>(dst + u * 8));
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(ot + (u / (RW / 8)) * OSTR + (u % (RW / 8)) * 8),
+                                  reinterpret_cast<u32x4 *>(dst + u * 8));
   }
   for (int h = tid; h < hg; h += nthreads) {
     p.ml[2 * (pbase + h)] = m_s[h];
