@@ -195,6 +195,27 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
 // ------------------------------------------------------------------ float32 stream
 // One workgroup per (split, head, sequence); four wavefronts take every fourth
 // token of the split, each with its own online-softmax state, combined at the end.
+// Reductions over aligned groups of N = 8 or 16 lanes with DPP lane swaps
+// (xor 1, xor 2, mirror within 8, mirror within 16).
+template <int CTRL, bool MAX>
+__device__ __forceinline__ float dpp_step(float x) {
+  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return MAX ? fmaxf(x, y) : x + y;
+}
+
+template <int N, bool MAX>
+__device__ __forceinline__ float dpp_reduce(float v) {
+  v = dpp_step<0xB1, MAX>(v);   // quad_perm [1,0,3,2]
+  v = dpp_step<0x4E, MAX>(v);   // quad_perm [2,3,0,1]
+  v = dpp_step<0x141, MAX>(v);  // row_half_mirror
+  if constexpr (N >= 16) v = dpp_step<0x140, MAX>(v);  // row_mirror
+  if constexpr (N == 32) {      // the neighbouring 16-lane row
+    const float y = __shfl_xor(v, 16, 64);
+    v = MAX ? fmaxf(v, y) : v + y;
+  }
+  return v;
+}
+
 template <int MAXJ>
 __global__ __launch_bounds__(256) void stream_f32_kernel(const float *__restrict__ C,
                                                          const float *__restrict__ qt,
@@ -221,24 +242,37 @@ __global__ __launch_bounds__(256) void stream_f32_kernel(const float *__restrict
   float m = -INFINITY, l = 0.f;
   const int64_t t0 = split * chunk;
   const int64_t t1 = min(L, t0 + chunk);
-  for (int64_t t = t0 + wave; t < t1; t += 4) {
-    const float *row = C + (static_cast<int64_t>(seq) * L + t) * r;
-    float c[MAXJ];
-    float s = 0.f;
+  // the wavefront's tokens t0 + wave, t0 + wave + 4, ... in batches of TB
+  // whose rows are requested together (rows past t1 are clamped and skipped)
+  constexpr int TB = 4;
+  for (int64_t tb = t0 + wave; tb < t1; tb += 4 * TB) {
+    float c[TB][MAXJ];
 #pragma unroll
-    for (int k = 0; k < MAXJ; ++k) {
-      const int j = lane + 64 * k;
-      c[k] = (j < r) ? row[j] : 0.f;
-      s = fmaf(c[k], qv[k], s);
+    for (int u = 0; u < TB; ++u) {
+      const int64_t t = min(tb + 4 * u, t1 - 1);
+      const float *row = C + (static_cast<int64_t>(seq) * L + t) * r;
+#pragma unroll
+      for (int k = 0; k < MAXJ; ++k) {
+        const int j = lane + 64 * k;
+        c[u][k] = (j < r) ? row[j] : 0.f;
+      }
     }
-    s = group_sum<64>(s);
-    const float mn = fmaxf(m, s);
-    const float alpha = exp2f(m - mn);
-    const float p = exp2f(s - mn);
-    l = fmaf(l, alpha, p);
 #pragma unroll
-    for (int k = 0; k < MAXJ; ++k) o[k] = fmaf(o[k], alpha, p * c[k]);
-    m = mn;
+    for (int u = 0; u < TB; ++u) {
+      if (tb + 4 * u >= t1) break;
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < MAXJ; ++k) s = fmaf(c[u][k], qv[k], s);
+      s = dpp_reduce<32, false>(s);
+      s += __shfl_xor(s, 32, 64);
+      const float mn = fmaxf(m, s);
+      const float alpha = exp2f(m - mn);
+      const float p = exp2f(s - mn);
+      l = fmaf(l, alpha, p);
+#pragma unroll
+      for (int k = 0; k < MAXJ; ++k) o[k] = fmaf(o[k], alpha, p * c[u][k]);
+      m = mn;
+    }
   }
 #pragma unroll
   for (int k = 0; k < MAXJ; ++k) {
@@ -382,27 +416,6 @@ __device__ __forceinline__ u32x4 i4_order(u32x4 v) {
 }
 // Column (within its group of eight) held at K position p of the int4 order.
 __device__ __forceinline__ int i4_column(int p) { return (p >> 1) + 4 * (p & 1); }
-
-// Reductions over aligned groups of N = 8 or 16 lanes with DPP lane swaps
-// (xor 1, xor 2, mirror within 8, mirror within 16).
-template <int CTRL, bool MAX>
-__device__ __forceinline__ float dpp_step(float x) {
-  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-  return MAX ? fmaxf(x, y) : x + y;
-}
-
-template <int N, bool MAX>
-__device__ __forceinline__ float dpp_reduce(float v) {
-  v = dpp_step<0xB1, MAX>(v);   // quad_perm [1,0,3,2]
-  v = dpp_step<0x4E, MAX>(v);   // quad_perm [2,3,0,1]
-  v = dpp_step<0x141, MAX>(v);  // row_half_mirror
-  if constexpr (N >= 16) v = dpp_step<0x140, MAX>(v);  // row_mirror
-  if constexpr (N == 32) {      // the neighbouring 16-lane row
-    const float y = __shfl_xor(v, 16, 64);
-    v = MAX ? fmaxf(v, y) : v + y;
-  }
-  return v;
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
@@ -1145,31 +1158,47 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(const uint16_
   }
 }
 
-// ------------------------------------------------------------------ merge
-// Workgroup (chunk jc of 128 latent rows, head h, 16 sequences):
+// ------------------------------------------------------------------ merge (float32 path)
+// Workgroup (chunk jc of kMergeRows latent rows, head h, 16 sequences):
 //   1. log-sum-exp weights of every split (one wavefront per sequence),
-//   2. merged O~ rows of the chunk (16 B partial loads),
+//   2. merged O~ rows of the chunk,
 //   3. the chunk's share of O~ W^u_v,h in float32 -> opj[jc][b][h][d].
+// Every thread requests its share of the W^u_v chunk first (batches of 16
+// independent loads, staged in LDS), and the partial rows of a batch of
+// splits together, so no thread walks W or the splits one load at a time.
 // W^u_v is read once per (chunk, head): the whole grid reads it once.
-template <typename PT, typename WT>
-__global__ __launch_bounds__(256) void merge_f32_kernel(const PT *__restrict__ opart,
-                                                    const float *__restrict__ ml,
-                                                    const WT *__restrict__ Wv,
-                                                    const float *__restrict__ wscale,
-                                                    float *__restrict__ opj, int b, int r,
-                                                    int heads, int d, int S) {
-  constexpr int BB = 16;
+constexpr int kMergeF32Batch = 8;
+
+__global__ __launch_bounds__(256) void merge_f32_kernel(const float *__restrict__ opart,
+                                                        const float *__restrict__ ml,
+                                                        const float *__restrict__ Wv,
+                                                        const float *__restrict__ wscale,
+                                                        float *__restrict__ opj, int b, int r,
+                                                        int heads, int d, int S) {
+  constexpr int BB = 16, NT = 256, WB = 16;
   extern __shared__ float fsm[];
   float *wts = fsm;                  // [BB][S]
-  float *mv = fsm + BB * S;          // [BB][kMergeRows]
+  float *mv = wts + BB * S;          // [BB][kMergeRows]
+  float *wl = mv + BB * kMergeRows;  // [kMergeRows][d]
   const int jc = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * BB;
   const int nbb = min(BB, b - b0);
   const int64_t E = static_cast<int64_t>(heads) * d;
   const int j0 = jc * kMergeRows;
   const int rows = min(kMergeRows, r - j0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = rows * d;   // W chunk elements, row-major [row][column]
 
-  for (int bi = wave; bi < nbb; bi += 4) {
+  // ---- W chunk: first batch requested now, stored after the weights
+  auto w_at = [&](int idx) {
+    const int e = min(idx, nw - 1);
+    return Wv + static_cast<int64_t>(j0 + e / d) * E + static_cast<int64_t>(h) * d + e % d;
+  };
+  float wv[WB];
+#pragma unroll
+  for (int k = 0; k < WB; ++k) wv[k] = *w_at(tid + NT * k);
+
+  // ---- split weights w_s = 2^(m_s - M) l_s / sum
+  for (int bi = wave; bi < nbb; bi += NT / 64) {
     const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
     float mx = -INFINITY;
     for (int s = lane; s < S; s += 64) mx = fmaxf(mx, ml[2 * (base + static_cast<int64_t>(s) * heads)]);
@@ -1185,91 +1214,66 @@ __global__ __launch_bounds__(256) void merge_f32_kernel(const PT *__restrict__ o
     const float inv = den > 0.f ? 1.f / den : 0.f;
     for (int s = lane; s < S; s += 64) wts[bi * S + s] *= inv;
   }
-  __syncthreads();
-
-  if constexpr (sizeof(PT) == 2) {
-    // r % 32 == 0 on this path: 8 consecutive rows per thread, 16-byte loads
-    const int bi = tid >> 4, jj0 = (tid & 15) * 8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (bi < nbb && jj0 < rows) {
-      const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
-      for (int s = 0; s < S; ++s) {
-        const float w = wts[bi * S + s];
-        if (w != 0.f) {
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(
-              opart + (base + static_cast<int64_t>(s) * heads) * r + j0 + jj0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
-            acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xFFFF0000u), acc[2 * e + 1]);
-          }
-        }
-      }
-    }
+  for (int k = 0; k < WB; ++k)
+    if (tid + NT * k < nw) wl[tid + NT * k] = wv[k];
+  for (int k0 = WB * NT; k0 < nw; k0 += WB * NT) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mv[bi * kMergeRows + jj0 + e] = acc[e];
-  } else {
-    for (int idx = tid; idx < BB * kMergeRows; idx += blockDim.x) {
-      const int bi = idx / kMergeRows, jj = idx % kMergeRows;
-      float acc = 0.f;
-      if (bi < nbb && jj < rows) {
-        const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
-        for (int s = 0; s < S; ++s) {
-          const float w = wts[bi * S + s];
-          if (w != 0.f) acc = fmaf(w, opart[(base + static_cast<int64_t>(s) * heads) * r + j0 + jj], acc);
-        }
-      }
-      mv[idx] = acc;
-    }
+    for (int k = 0; k < WB; ++k) wv[k] = *w_at(k0 + tid + NT * k);
+#pragma unroll
+    for (int k = 0; k < WB; ++k)
+      if (k0 + tid + NT * k < nw) wl[k0 + tid + NT * k] = wv[k];
   }
   __syncthreads();
 
-  // thread -> column i of the head, sequences g, g + groups, ...
-  const int groups = max(1, 256 / d);
-  const int i = tid % d, g = tid / d;
-  if (g < groups && i < d) {
-    float acc[BB];
+  // ---- merged O~ rows: batches of splits whose partial rows load together
+  for (int idx = tid; idx < BB * kMergeRows; idx += NT) {
+    const int bi = idx / kMergeRows, jj = idx % kMergeRows;
+    float acc = 0.f;
+    if (bi < nbb && jj < rows) {
+      const int64_t base = static_cast<int64_t>(b0 + bi) * S * heads + h;
+      for (int s0 = 0; s0 < S; s0 += kMergeF32Batch) {
+        float v[kMergeF32Batch];
 #pragma unroll
-    for (int k = 0; k < BB; ++k) acc[k] = 0.f;
-    const WT *wcol = Wv + static_cast<int64_t>(j0) * E + h * d + i;
-    int jj = 0;
-    for (; jj + 4 <= rows; jj += 4) {
-      float w[4];
+        for (int k = 0; k < kMergeF32Batch; ++k)
+          v[k] = opart[(base + static_cast<int64_t>(min(s0 + k, S - 1)) * heads) * r + j0 + jj];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if constexpr (sizeof(WT) == 2)
-          w[u] = bf16_to_f32(wcol[(jj + u) * E]);
-        else
-          w[u] = static_cast<float>(wcol[(jj + u) * E]);
-      }
-#pragma unroll
-      for (int k = 0; k < BB; ++k) {
-        const int bi = g + k * groups;
-        if (bi < nbb) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[k] = fmaf(mv[bi * kMergeRows + jj + u], w[u], acc[k]);
-        }
+        for (int k = 0; k < kMergeF32Batch; ++k)
+          if (s0 + k < S) acc = fmaf(wts[bi * S + s0 + k], v[k], acc);
       }
     }
-    for (; jj < rows; ++jj) {
-      float w;
-      if constexpr (sizeof(WT) == 2)
-        w = bf16_to_f32(wcol[jj * E]);
-      else
-        w = static_cast<float>(wcol[jj * E]);
+    mv[idx] = acc;
+  }
+  __syncthreads();
+
+  // ---- thread -> column i of the head and rows rg, rg + RG, ... of the
+  // chunk for every sequence; the RG row groups are summed through LDS
+  // (fixed order) after a barrier.  The shares reuse the W chunk's LDS.
+  const int RG = NT / d;             // 2 (d = 128) or 4 (d = 64)
+  const int i = tid % d, rg = tid / d;
+  float acc[BB];
 #pragma unroll
-      for (int k = 0; k < BB; ++k) {
-        const int bi = g + k * groups;
-        if (bi < nbb) acc[k] = fmaf(mv[bi * kMergeRows + jj], w, acc[k]);
-      }
-    }
-    const float sc = wscale ? wscale[h * d + i] : 1.f;
+  for (int k = 0; k < BB; ++k) acc[k] = 0.f;
+  for (int jj = rg; jj < rows; jj += RG) {
+    const float w = wl[jj * d + i];
+    if (nbb == BB) {
 #pragma unroll
-    for (int k = 0; k < BB; ++k) {
-      const int bi = g + k * groups;
-      if (bi < nbb)
-        opj[((static_cast<int64_t>(jc) * b + b0 + bi) * heads + h) * d + i] = acc[k] * sc;
+      for (int k = 0; k < BB; ++k) acc[k] = fmaf(mv[k * kMergeRows + jj], w, acc[k]);
+    } else {
+      for (int k = 0; k < nbb; ++k) acc[k] = fmaf(mv[k * kMergeRows + jj], w, acc[k]);
     }
+  }
+  __syncthreads();                   // every thread is done with the W chunk
+  float *red = wl;                   // [RG][BB][d]
+#pragma unroll
+  for (int k = 0; k < BB; ++k)
+    if (k < nbb) red[(rg * BB + k) * d + i] = acc[k];
+  __syncthreads();
+  const float sc = wscale ? wscale[h * d + i] : 1.f;
+  for (int k = rg; k < nbb; k += RG) {
+    float v = 0.f;
+    for (int g = 0; g < RG; ++g) v += red[(g * BB + k) * d + i];
+    opj[((static_cast<int64_t>(jc) * b + b0 + k) * heads + h) * d + i] = v * sc;
   }
 }
 
@@ -1408,8 +1412,9 @@ hipError_t launch_absorb_t(const DecodeArgs &a, OT *qt, hipStream_t s) {
 hipError_t launch_merge_f32(const DecodeArgs &a, const DecodePlan &p, const float *opart,
                             const float *ml, float *opj, hipStream_t s) {
   const int JC = (a.r + kMergeRows - 1) / kMergeRows;
-  const size_t lds = (static_cast<size_t>(16) * p.splits + 16 * kMergeRows) * sizeof(float);
-  auto kern = merge_f32_kernel<float, float>;
+  const size_t lds = (static_cast<size_t>(16) * p.splits + 16 * kMergeRows +
+                      static_cast<size_t>(kMergeRows) * a.d) * sizeof(float);
+  auto kern = merge_f32_kernel;
   hipError_t e = set_dynamic_lds(reinterpret_cast<const void *>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(JC, a.heads, (a.b + 15) / 16), dim3(256), lds, s>>>(
@@ -1561,7 +1566,7 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
     } else {
       const int64_t per = static_cast<int64_t>(b) * p.head_groups;
       S = std::max<int64_t>(1, kNumCU / std::max<int64_t>(per, 1));
-      S = std::max<int64_t>(1, std::min<int64_t>(S, (L + 63) / 64));
+      S = std::max<int64_t>(1, std::min<int64_t>(S, (L + 15) / 16));
       S = std::min<int64_t>(S, max_splits);
       p.chunk = (L + S - 1) / S;
     }
