@@ -192,11 +192,9 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
         u32x2{pack_bf16x2(acc[0] * scale, acc[1] * scale), pack_bf16x2(acc[2] * scale, acc[3] * scale)};
 }
 
-// ------------------------------------------------------------------ float32 stream
-// One workgroup per (split, head, sequence); four wavefronts take every fourth
-// token of the split, each with its own online-softmax state, combined at the end.
-// Reductions over aligned groups of N = 8 or 16 lanes with DPP lane swaps
-// (xor 1, xor 2, mirror within 8, mirror within 16).
+// Reductions over aligned groups of N = 8, 16 or 32 lanes: DPP lane swaps
+// (xor 1, xor 2, mirror within 8, mirror within 16), then for 32 one swap of
+// neighbouring 16-lane rows.
 template <int CTRL, bool MAX>
 __device__ __forceinline__ float dpp_step(float x) {
   const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -216,6 +214,9 @@ __device__ __forceinline__ float dpp_reduce(float v) {
   return v;
 }
 
+// ------------------------------------------------------------------ float32 stream
+// One workgroup per (split, head, sequence); four wavefronts take every fourth
+// token of the split, each with its own online-softmax state, combined at the end.
 template <int MAXJ>
 __global__ __launch_bounds__(256) void stream_f32_kernel(const float *__restrict__ C,
                                                          const float *__restrict__ qt,
