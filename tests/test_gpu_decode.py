@@ -167,8 +167,22 @@ def test_quantised_cache_sharpened(bits, r, L, b, heads, factor):
     _quantised_cache(bits, r, L, b, heads, "i8", factor, row_tol=4e-2 if factor <= 30 else 1e-1)
 
 
-def _quantised_cache(bits, r, L, b, heads, wu, factor, row_tol=None):
-    d = 128
+@pytest.mark.parametrize("bits,r,L,b,heads,d", [
+    (4, 1536, 300, 2, 32, 128),   # six wavefronts of 256 columns (two scale groups each)
+    (8, 256, 100, 3, 20, 128),    # 20 heads: a partly filled second 16-head block
+    (4, 512, 70, 17, 8, 64),      # d = 64, more than 16 sequences (a second block in absorb and merge)
+    (8, 1024, 65, 1, 16, 64),     # d = 64, one token past a 64-token tile
+    (4, 256, 129, 2, 33, 128),    # 33 heads: two head groups, one head in the last block
+    (8, 2304, 50, 1, 40, 128),    # the widest int8 latent, 40 heads in three head groups
+    (4, 384, 40, 2, 24, 64),      # fewer tokens than a tile, three wavefronts
+], ids=lambda v: str(v))
+def test_quantised_cache_shapes(bits, r, L, b, heads, d):
+    """Shape sweep of the quantised caches: scale groups per wavefront, partly
+    filled head blocks, several head groups, d = 64, batches over 16."""
+    _quantised_cache(bits, r, L, b, heads, "i8", 1.0, d=d)
+
+
+def _quantised_cache(bits, r, L, b, heads, wu, factor, row_tol=None, d=128):
     say(f"case: int{bits} cache r={r} L={L} b={b} heads={heads} W^u {wu} query x{factor}")
     codes, scales, Wk_q, Wk_s, Wv_q, Wv_s, qv = _quant_case(r, L, b, heads, d, bits, seed=r + L)
     if factor != 1.0:
