@@ -171,9 +171,14 @@ qsvd_status_t qsvd_pack_weight(const void *W, qsvd_dtype_t dt, int32_t rows, int
  *     BF16 : q, C, W^u BF16; O BF16 or F32 (bf16 MFMA, float32 accumulation).
  *     I4/I8: q BF16, W^u BF16 or I8; O BF16 or F32.
  *   Constraints: E == heads * d, heads <= 256, L >= 1, 1 <= b <= 65535;
- *   F32: 1 <= r <= 4096;  other caches: r % 32 == 0 and r / W <= 288, where W
- *   is the largest of 8, 4, 2, 1 with r % (32 W) == 0 (so r <= 2304 for
- *   r % 256 == 0);  I4: r % 128 == 0.  d is 64 or 128 (QSVD_ERR_UNSUPPORTED otherwise).
+ *   F32: 1 <= r <= 4096;  other caches: the latent columns are split over W
+ *   wavefronts of r / W columns each, W the largest of 8, 7, ..., 1 with
+ *   r % (W g) == 0 for the load granule g (BF16: 32 columns, I8: 64, I4: 128),
+ *   and r / W must be at most 384 (so r <= 3072; e.g. 768, 1536, 2304 and
+ *   3072 qualify for all three formats, 2560 not for I4).
+ *   qsvd_decode_workspace_bytes returns 0 for a width that does not qualify.
+ *   d is 64 or 128
+ *   (QSVD_ERR_UNSUPPORTED otherwise).
  */
 size_t qsvd_decode_workspace_bytes(int32_t b, int64_t L, int32_t r, int32_t heads, int32_t d,
                                    qsvd_dtype_t c_dtype, int32_t splits);

@@ -233,3 +233,18 @@ def test_decode_headwise_validation():
     assert q.qsvd_decode_headwise_workspace_bytes(2, 300, 6, 64, 64, 32, 0) == 0
     assert st_hw(wsb=need - 1) == -3
     assert st_hw(ws=None) == -3
+
+
+def test_latent_width_rule_matches_the_header():
+    """The header's rule for the latent widths the MFMA paths accept: W the
+    largest of 8..1 with r % (W g) == 0 (g = 32 / 64 / 128 columns for bf16 /
+    int8 / int4 caches) and at most 384 columns per wavefront."""
+    def accepted(r, g):
+        for W in range(8, 0, -1):
+            if r % (W * g) == 0:
+                return r // W <= 384
+        return False
+    for r in range(32, 4097, 32):
+        for dt, g in ((q.BF16, 32), (q.I8, 64), (q.I4, 128)):
+            ok = q.qsvd_decode_workspace_bytes(2, 100, r, 8, 128, dt, 0) > 0
+            assert ok == accepted(r, g), (r, dt)

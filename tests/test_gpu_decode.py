@@ -90,6 +90,37 @@ def test_bf16_shapes(shape):
     check_rows(got, oracle_out(cs), TOL_BF16, "bf16")
 
 
+# Latent widths whose wavefront count is not a power of two (r = 32 NKB W with
+# W the largest of 8..1 dividing r / 32 within 12 K blocks per wavefront) and
+# the widest accepted latents (12 K blocks per wavefront).
+WIDTH_SHAPES = [
+    # c_dtype, r, heads, b, L
+    ("bf16", 160, 8, 2, 70),     # W = 5
+    ("bf16", 224, 8, 2, 70),     # W = 7
+    ("bf16", 352, 8, 2, 70),     # W = 1 (11 K blocks in one wavefront)
+    ("bf16", 480, 8, 2, 70),     # W = 5, 3 K blocks
+    ("bf16", 2560, 32, 2, 150),  # W = 8, 10 K blocks
+    ("bf16", 3072, 32, 2, 150),  # W = 8, 12 K blocks (16-token tiles)
+    ("i8", 320, 8, 2, 70),       # W = 5
+    ("i8", 2560, 32, 2, 150),
+    ("i8", 3072, 16, 2, 150),
+    ("i4", 3072, 16, 2, 150),
+]
+
+
+@pytest.mark.parametrize("case", WIDTH_SHAPES, ids=lambda c: "{}-r{}-h{}".format(c[0], c[1], c[2]))
+def test_latent_widths(case):
+    cdt, r, heads, b, L = case
+    if cdt == "bf16":
+        say(f"case: latent width bf16 r={r} heads={heads} b={b} L={L}")
+        cs = synth.decode_case(heads * 128, heads, 128, r, b, L, dtype="bf16",
+                               hadamard=128 if r % 128 == 0 else 0, p=0.5, seed=r + heads)
+        got = decode_case_on_gpu(cs)
+        check_rows(got, oracle_out(cs), TOL_BF16, f"r={r}")
+    else:
+        _quantised_cache(4 if cdt == "i4" else 8, r, L, b, heads, "i8", 1.0)
+
+
 @pytest.mark.parametrize("factor", [1.0, 30.0, 300.0])
 def test_bf16_sharpened_softmax(factor):
     """Sharpened queries (score spread of several units) exercise the online

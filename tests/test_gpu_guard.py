@@ -75,6 +75,10 @@ SHARED = [
     ("int4", q.I4, 4096, 32, 128, 768, 2, 1000, 0),
     ("int4-splits", q.I4, 512, 4, 128, 128, 1, 5, 3),
     ("two-pass", q.BF16, 5120, 40, 128, 2304, 2, 500, 0),
+    ("bf16-five-waves", q.BF16, 1024, 8, 128, 160, 2, 70, 0),
+    ("bf16-one-wave", q.BF16, 1024, 8, 128, 352, 2, 70, 0),
+    ("bf16-r3072", q.BF16, 4096, 32, 128, 3072, 1, 150, 0),
+    ("int4-r3072", q.I4, 2048, 16, 128, 3072, 1, 150, 0),
 ]
 
 
