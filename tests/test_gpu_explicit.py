@@ -53,6 +53,9 @@ SHAPES = [
     (2048, 16, 1536, 1, 77),    # r of the 7B shape, one partial tile
     (512, 4, 128, 3, 1),        # a single cached latent
     (1024, 8, 256, 3, 2500),    # two groups of eight tiles per sequence, the last one partial
+    (512, 4, 64, 2, 300),       # r = 64: a single 128-byte K stage
+    (1024, 8, 192, 1, 513),     # r = 192: an odd number of K stages
+    (4096, 32, 3072, 1, 100),   # r = 3072: the longest K loop of the tests
 ]
 
 
@@ -61,7 +64,8 @@ SHAPES = [
 def test_explicit_matches_oracle(shape, rope):
     E, heads, r, b, L = shape
     say(f"case: explicit E={E} heads={heads} r={r} b={b} L={L} rope={rope}")
-    cs = synth.decode_case(E, heads, 128, r, b, L, dtype="bf16", hadamard=128, seed=E + L)
+    cs = synth.decode_case(E, heads, 128, r, b, L, dtype="bf16", hadamard=128 if r % 128 == 0 else 0,
+                           seed=E + L)
     got = run_explicit(cs, rope)
     check_rows(got, oracle_out(cs, rope), TOL, "explicit")
 
