@@ -197,11 +197,13 @@ def main():
 
     # plain device copy of a known size: its FETCH_SIZE / WRITE_SIZE counters give the
     # factor that turns the counters of the decode kernels into HBM bytes
+    # The same copies, timed, give the copy ceiling (bytes read + written per second) that
+    # the HBM legs are also reported against.
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    copy_ms = timed(lambda i: dst.copy_(src), 3, 1)
+    copy_gbps = 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9
+    log(f"[bench] 1 GiB device copy: {copy_ms * 1e3:.0f} us = {copy_gbps:.0f} GB/s read + written")
     del src, dst
 
     stream_ms = kern.get("decode_stream", float("nan"))
@@ -320,6 +322,10 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cs, O)
 
+    for leg in [headwise] + (list(configs.values()) if configs else []):
+        if leg and leg.get("roofline", {}).get("bound") == "hbm":
+            leg["roofline"]["frac_of_copy_ceiling"] = round(leg["roofline"]["achieved"] / copy_gbps, 4)
+
     out = {
         "metric": "decode tokens/s + HBM GB/s (E=4096,r=1536,b=16,L=8192); prefill proj TOPS",
         "value": round(b / (ms * 1e-3), 1),
@@ -346,7 +352,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_stream", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": cache_bytes},
+                     "algorithmic_bytes": cache_bytes,
+                     "copy_ceiling_gbps": round(copy_gbps, 1),
+                     "frac_of_copy_ceiling": round(achieved / copy_gbps, 4)},
         "cpu_baseline": cpu,
         "tiny_fp32": tiny,
         "prefill": prefill,
