@@ -1504,10 +1504,11 @@ bool mfma_shape(int r, int heads, int c_dtype, MfmaShape *out) {
     }();
     if (tile_env == 16 && s.NHB == 1) s.T = 16;
     if (tile_env == 32 && nkb <= 10 && stream_lds_bytes(W, s.NHB, nkb, 32, kind) <= kMaxLds) s.T = 32;
-    // quantised 64-token tiles stage in few registers: two tiles of loads in
-    // flight (tuning override QSVD_STREAM_DEPTH = 1..3)
+    // tiles of loads in flight: two for 16-token tiles, else one.  Quantised
+    // 64-token tiles could stage two, but the second adds register pressure
+    // and no speed (W8A4 shape: 36.6 vs 36.8 us int4, 38.9 vs 39.1 us int8);
+    // tuning override QSVD_STREAM_DEPTH = 1..3
     s.D = (s.T == 16) ? 2 : 1;
-    if (s.T == 64 && stream_depth_fits(kind == 1, s.NHB, nkb, 2)) s.D = 2;
     static const int depth_env = [] {
       const char *e = std::getenv("QSVD_STREAM_DEPTH");
       return e ? std::atoi(e) : 0;
