@@ -587,7 +587,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
   // Quantised caches: the score and value products run on the exact codes
   // plus a constant offset (136 for int4, 128 for int8) and the scales are
   // applied to the results.  For a wavefront and scale group g:
-  //   partial score  s_t = scale_{t,g} (sum_j (off + c_tj) q~_j - off sum_j q~_j)
+  //   partial score  s_t = scale_{t,g} (-off sum_j q~_j + sum_j (off + c_tj) q~_j)
   //   value product  O~_j = sum_t P'_t (off + c_tj) - off sum_t P'_t,
   //                  P'_t = bf16(p_t scale_{t,g})
   // koff holds off * sum_j q~_j (a product of ones with the Q~ operands) and
@@ -665,11 +665,20 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
           for (int g = 0; g < NG; ++g) ssc[g * T + tb * 16 + li] = sscale[bf][tb][g * (NLD / NG)];
         }
       }
+      // quantised caches start each group's sum at -off sum_j q~_j, so that
+      // the products leave sum_j c_tj q~_j (no subtraction per element)
       f32x4 sacc[NG][NHB];
 #pragma unroll
       for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) sacc[g][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int hb = 0; hb < NHB; ++hb) {
+          if constexpr (CT != CT_BF16) {
+            const float k0 = -koff[g][hb];
+            sacc[g][hb] = f32x4{k0, k0, k0, k0};
+          } else {
+            sacc[g][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -695,7 +704,7 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
           for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float v = (sacc[g][hb][e] - koff[g][hb]) * s4[e];
+              const float v = sacc[g][hb][e] * s4[e];
               part[hb][e] = g == 0 ? v : part[hb][e] + v;
             }
         }
