@@ -52,6 +52,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kNumCU = 256;  // MI355X compute units
 constexpr int kMergeRows = 128;
 constexpr int kMaxSplits = 1024;
+// The stream kernel's running softmax maximum moves only when a tile's
+// maximum exceeds it by more than this (log2 units): p stays below 2^8.
+constexpr float kRescaleSlack = 8.f;
 
 enum CType : int { CT_BF16 = 0, CT_I4 = 1, CT_I8 = 2 };
 
@@ -758,7 +761,10 @@ __global__ __launch_bounds__(512) void stream_mfma_kernel(StreamParams p) {
           mx = fmaxf(mx, sc[e]);
         }
         mx = dpp_reduce<8, true>(mx);
-        const float m_new = fmaxf(m_old, mx);
+        // lazy running maximum: kept until the tile's maximum exceeds it by
+        // more than kRescaleSlack (log2 units), so p <= 2^kRescaleSlack and O~
+        // is rescaled only on such tiles; the result is the same function
+        const float m_new = mx > m_old + kRescaleSlack ? mx : m_old;
         const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
         uint32_t pp[TPI / 2];
         float ps = 0.f;
