@@ -308,6 +308,156 @@ __global__ __launch_bounds__(256) void stream_f32_kernel(const float *__restrict
   }
 }
 
+// ------------------------------------------------------------------ float32, one launch
+// Small float32 problems take the whole step in one launch (the four launches
+// of the split path cost more than the work).  Workgroup (head h, sequence),
+// 16 wavefronts:
+//   1. q~ = scale log2e W^u_k,h q_h: wavefront w computes latent rows w,
+//      w + 16, ... (one 64-lane dot product each, every row requested first),
+//   2. wavefront w streams tokens w, w + 16, ... with its own online softmax,
+//      TB rows requested together,
+//   3. the 16 states are combined in LDS by log-sum-exp weights (fixed order),
+//   4. O = (O~ / l) W^u_v,h: thread (column c, row group g) sums the rows
+//      g, g + G, ..., and the G row groups are summed in LDS.
+constexpr int kFusedWaves = 16;
+
+template <int MAXJ>
+__global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
+    const float *__restrict__ q, const float *__restrict__ C, const float *__restrict__ Wk,
+    const float *__restrict__ Wv, float *__restrict__ O, int64_t L, int r, int heads, int d,
+    float scale) {
+  constexpr int NW = kFusedWaves, NT = 64 * NW;
+  constexpr int RPW = (64 * MAXJ + NW - 1) / NW;   // latent rows per wavefront in step 1
+  constexpr int TB = 8;                            // token rows requested together
+  extern __shared__ float fs[];
+  float *qs = fs;               // [r] q~
+  float *wo = qs + r;           // [NW][r] per-wavefront O~
+  float *wm = wo + NW * r;      // [NW] running maxima
+  float *wl = wm + NW;          // [NW] running sums
+  float *ot = wl + NW;          // [r] O~ / l
+  float *red = ot + r;          // [NT] projection shares
+  const int h = blockIdx.x, seq = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t E = static_cast<int64_t>(heads) * d;
+
+  // ---- 1. absorbed query
+  {
+    const float *qh = q + (static_cast<int64_t>(seq) * heads + h) * d;
+    const float q0 = lane < d ? qh[lane] : 0.f;
+    const float q1 = lane + 64 < d ? qh[lane + 64] : 0.f;
+    float w0[RPW], w1[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int k = min(wave + NW * i, r - 1);
+      const float *row = Wk + static_cast<int64_t>(k) * E + static_cast<int64_t>(h) * d;
+      w0[i] = lane < d ? row[lane] : 0.f;
+      w1[i] = lane + 64 < d ? row[lane + 64] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      float v = fmaf(w1[i], q1, w0[i] * q0);
+      v = dpp_reduce<32, false>(v);
+      v += __shfl_xor(v, 32, 64);
+      const int k = wave + NW * i;
+      if (lane == 0 && k < r) qs[k] = v * scale;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. this wavefront's tokens
+  float qv[MAXJ], o[MAXJ];
+#pragma unroll
+  for (int k = 0; k < MAXJ; ++k) {
+    const int j = lane + 64 * k;
+    qv[k] = j < r ? qs[j] : 0.f;
+    o[k] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int64_t tb = wave; tb < L; tb += NW * TB) {
+    float c[TB][MAXJ];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int64_t t = min(tb + NW * u, L - 1);
+      const float *row = C + (static_cast<int64_t>(seq) * L + t) * r;
+#pragma unroll
+      for (int k = 0; k < MAXJ; ++k) {
+        const int j = lane + 64 * k;
+        c[u][k] = j < r ? row[j] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      if (tb + NW * u >= L) break;
+      float sc = 0.f;
+#pragma unroll
+      for (int k = 0; k < MAXJ; ++k) sc = fmaf(c[u][k], qv[k], sc);
+      sc = dpp_reduce<32, false>(sc);
+      sc += __shfl_xor(sc, 32, 64);
+      const float mn = fmaxf(m, sc);
+      const float alpha = exp2f(m - mn);
+      const float pe = exp2f(sc - mn);
+      l = fmaf(l, alpha, pe);
+#pragma unroll
+      for (int k = 0; k < MAXJ; ++k) o[k] = fmaf(o[k], alpha, pe * c[u][k]);
+      m = mn;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MAXJ; ++k) {
+    const int j = lane + 64 * k;
+    if (j < r) wo[wave * r + j] = o[k];
+  }
+  if (lane == 0) {
+    wm[wave] = m;
+    wl[wave] = l;
+  }
+  __syncthreads();
+
+  // ---- 3. combine the wavefronts (L >= 1: the maximum is finite)
+  {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);
+    float f[NW], lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      f[w] = exp2f(wm[w] - M);   // 0 for a wavefront without tokens
+      lt = fmaf(wl[w], f[w], lt);
+    }
+    const float inv = 1.f / lt;
+    for (int j = tid; j < r; j += NT) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc = fmaf(wo[w * r + j], f[w], acc);
+      ot[j] = acc * inv;
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. output projection
+  const int G = NT / d;
+  const int cc = tid % d, g = tid / d;
+  float acc = 0.f;
+  for (int k0 = g; k0 < r; k0 += 4 * G) {
+    float wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = min(k0 + G * u, r - 1);
+      wv[u] = Wv[static_cast<int64_t>(k) * E + static_cast<int64_t>(h) * d + cc];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + G * u < r) acc = fmaf(ot[k0 + G * u], wv[u], acc);
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < d) {
+    float v = 0.f;
+    for (int gg = 0; gg < G; ++gg) v += red[gg * d + tid];
+    O[(static_cast<int64_t>(seq) * heads + h) * d + tid] = v;
+  }
+}
+
 // ------------------------------------------------------------------ MFMA stream
 struct StreamParams {
   const uint8_t *C;
@@ -1588,6 +1738,10 @@ DecodePlan plan_decode(int b, int64_t L, int r, int heads, int d, int c_dtype, i
       p.chunk = (L + S - 1) / S;
     }
     p.splits = static_cast<int>((L + p.chunk - 1) / p.chunk);
+    // small problems in one launch: at most 64 tokens per wavefront and one
+    // round of workgroups; a caller's explicit split count keeps the split path
+    p.fused = splits == 0 && r <= 256 && L <= 64 * kFusedWaves &&
+              static_cast<int64_t>(b) * heads <= kNumCU;
   }
   // merge chunk: the fewest rounds of workgroups over the compute units, then
   // the most workgroups (smallest chunk) within that many rounds
@@ -1629,6 +1783,27 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
   const size_t ml_bytes = align256(static_cast<size_t>(a.b) * p.splits * a.heads * 2 * sizeof(float));
   float *opj = reinterpret_cast<float *>(ws + p.qt_bytes + opart_bytes + ml_bytes);
   hipError_t e;
+
+  if (p.fused) {
+    LaunchTimer t("decode_fused", s);
+    const int maxj = (a.r + 63) / 64;
+    const size_t lds = (static_cast<size_t>(a.r) * (kFusedWaves + 2) + 2 * kFusedWaves + 64 * kFusedWaves) *
+                       sizeof(float);
+    const dim3 grid(a.heads, a.b), block(64 * kFusedWaves);
+    const auto *q = static_cast<const float *>(a.q);
+    const auto *C = static_cast<const float *>(a.C);
+    const auto *Wk = static_cast<const float *>(a.Wu_k);
+    const auto *Wv = static_cast<const float *>(a.Wu_v);
+    auto *O = static_cast<float *>(a.O);
+    const float scale = a.softmax_scale * kLog2e;
+    switch (maxj) {
+      case 1: decode_f32_fused_kernel<1><<<grid, block, lds, s>>>(q, C, Wk, Wv, O, a.L, a.r, a.heads, a.d, scale); break;
+      case 2: decode_f32_fused_kernel<2><<<grid, block, lds, s>>>(q, C, Wk, Wv, O, a.L, a.r, a.heads, a.d, scale); break;
+      case 3: decode_f32_fused_kernel<3><<<grid, block, lds, s>>>(q, C, Wk, Wv, O, a.L, a.r, a.heads, a.d, scale); break;
+      default: decode_f32_fused_kernel<4><<<grid, block, lds, s>>>(q, C, Wk, Wv, O, a.L, a.r, a.heads, a.d, scale); break;
+    }
+    return hipGetLastError();
+  }
 
   // ---- absorb
   {

@@ -154,6 +154,7 @@ struct DecodePlan {
   int head_groups;   // workgroups per (sequence, split) along heads
   int group_heads;   // heads per head group
   bool mfma;         // bf16 / quantised MFMA stream kernel (else float32 kernel)
+  bool fused;        // float32 path in one launch (small problems, library-chosen splits)
   bool wide;         // two-pass decode (score pass + value pass) instead of the stream kernel
   WidePlanInfo wp;   // its chunking (wide only)
   int rw;            // columns per partial block of the split partials

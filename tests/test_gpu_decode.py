@@ -65,6 +65,29 @@ def test_fp32_split_invariance(L, splits):
     assert oracle.rel_l2(got, oracle_out(cs)) <= TOL_F32
 
 
+@pytest.mark.parametrize("shape", [
+    # E, heads, d, r, b, L: shapes the library runs in one launch (library-chosen splits)
+    (256, 4, 64, 96, 1, 512),      # the tiny config's geometry
+    (512, 4, 128, 256, 3, 1024),   # the widest latent and the longest cache of the one-launch path
+    (128, 2, 64, 40, 2, 5),        # fewer tokens than wavefronts
+    (1024, 16, 64, 200, 2, 1),     # a single cached latent
+    (768, 6, 128, 130, 2, 333),    # r not a multiple of 64
+], ids=lambda s: "E{}h{}d{}r{}b{}L{}".format(*s))
+def test_fp32_one_launch_matches_split_path(shape):
+    """Small float32 problems run as one launch per step when the library
+    chooses the splits; the same step with explicit splits takes the split
+    path.  Both match the oracle and each other."""
+    E, heads, d, r, b, L = shape
+    say(f"case: fp32 one launch {shape}")
+    cs = synth.decode_case(E, heads, d, r, b, L, dtype="f32", seed=E + r + L)
+    ref = oracle_out(cs)
+    one = decode_case_on_gpu(cs)
+    split = decode_case_on_gpu(cs, splits=3)
+    check_rows(one, ref, TOL_F32, "one launch")
+    check_rows(split, ref, TOL_F32, "split path")
+    assert oracle.rel_l2(one, split) <= TOL_F32
+
+
 # ------------------------------------------------------------------ bf16 path
 BF16_SHAPES = [
     # E, heads, d, r, b, L
