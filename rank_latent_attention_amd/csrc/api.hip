@@ -527,7 +527,8 @@ qsvd_status_t decode_attn_checked(const void *q, qsvd_dtype_t q_dtype, const voi
     return fail(QSVD_ERR_INVALID, "decode: softmax_scale must be positive and finite");
   if (!q || !C || !Wu_k || !Wu_v || !O) return fail(QSVD_ERR_INVALID, "decode: NULL pointer");
   if (!aligned16(q) || !aligned16(C) || !aligned16(Wu_k) || !aligned16(Wu_v) || !aligned16(O) ||
-      (c_scales && !aligned4(c_scales)) || (workspace && !aligned16(workspace)))
+      (c_scales && !aligned4(c_scales)) || (wu_scale_k && !aligned16(wu_scale_k)) ||
+      (wu_scale_v && !aligned16(wu_scale_v)) || (workspace && !aligned16(workspace)))
     return fail(QSVD_ERR_INVALID, "decode: misaligned pointer");
   const DecodePlan plan = plan_decode(b, L, r, heads, d, c_dtype, splits);
   if (need) {

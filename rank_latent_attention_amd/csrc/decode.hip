@@ -154,20 +154,29 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
       }
     }
   }
+  // int8 W^u_k: the column scales of this lane's q elements, requested with
+  // the operands (one memory round trip for the whole workgroup)
+  f32x4 sv[DK][2];
+  if constexpr (sizeof(WT) == 1) {
+#pragma unroll
+    for (int k = 0; k < DK; ++k) {
+      sv[k][0] = *reinterpret_cast<const f32x4 *>(wscale + h * d + 32 * k + kq);
+      sv[k][1] = *reinterpret_cast<const f32x4 *>(wscale + h * d + 32 * k + kq + 4);
+    }
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < DK; ++k) {
-    const int i = 32 * k + kq;
     u32x4 a = av[k], w = bv[k];
     // int8 W^u_k: q times the column scales, carried as a bf16 pair
     // (head + tail, about 16 significant bits) so that the product keeps
     // the precision of q itself
     u32x4 a_tail = {0u, 0u, 0u, 0u};
-    if (wscale) {
+    if constexpr (sizeof(WT) == 1) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(a[e] << 16) * wscale[h * d + i + 2 * e];
-        const float hi = __uint_as_float(a[e] & 0xFFFF0000u) * wscale[h * d + i + 2 * e + 1];
+        const float lo = __uint_as_float(a[e] << 16) * sv[k][e >> 1][2 * (e & 1)];
+        const float hi = __uint_as_float(a[e] & 0xFFFF0000u) * sv[k][e >> 1][2 * (e & 1) + 1];
         a[e] = pack_bf16x2(lo, hi);
         a_tail[e] = pack_bf16x2(lo - __uint_as_float(a[e] << 16), hi - __uint_as_float(a[e] & 0xFFFF0000u));
       }
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
     // lane ends with 4 consecutive rows j0 + 4 g + (0..3) of sequence b0 + i
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                   __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
-    if (wscale)
+    if constexpr (sizeof(WT) == 1)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                     __builtin_bit_cast(bf16x8, a_tail), acc, 0, 0, 0);
   }
@@ -1206,6 +1215,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(const uint16_
   const uint16_t *psrc = opart + (static_cast<int64_t>(pseq) * S * (r / RW) + jrow / RW) * heads * RW +
                          static_cast<int64_t>(h) * RW + jrow % RW;
   const int64_t sstride = static_cast<int64_t>(heads) * r;
+  // int8 W^u_v: the column scale of this lane's output column in the
+  // product below (column block = wavefront, d <= 128), requested now
+  float sc0 = 1.f;
+  if constexpr (sizeof(WT) == 1)
+    if (wave < d / 16) sc0 = wscale[static_cast<int64_t>(h) * d + wave * 16 + (lane & 15)];
   u32x4 pv[kMergeBatch];
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) {
@@ -1315,7 +1329,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(const uint16_
                                                     acc, 0, 0, 0);
     }
     const int col = nb * 16 + li;
-    const float sc = wscale ? wscale[static_cast<int64_t>(h) * d + col] : 1.f;
+    float sc = sc0;
+    if constexpr (sizeof(WT) == 1)
+      if (nb != wave) sc = wscale[static_cast<int64_t>(h) * d + col];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int bo = 4 * lg + e;
