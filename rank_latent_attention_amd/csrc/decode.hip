@@ -60,6 +60,15 @@ enum CType : int { CT_BF16 = 0, CT_I4 = 1, CT_I8 = 2 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resource over [base, base + bytes): loads past the end return zero
+// without a branch (and without touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(n), 0x00020000);
+}
+
+
 // ------------------------------------------------------------------ absorb
 // q~[b][h][j] = scale * sum_i Wk[j][h d + i] * q[b][h][i].  One workgroup owns
 // 16 rows j of one head; 16 lanes split the d-wide row segment.
@@ -138,20 +147,25 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
   const int bb = b0 + (lane & 15);
   const int j = j0 + (lane & 15);
   const int kq = (lane >> 4) * 8;
+  // branch-free operand loads: sequences past b and rows past r lie outside
+  // the resources (based at the workgroup's first sequence and row) and read
+  // as zero, so every load is in flight before the first wait
+  const int jb0 = blockIdx.x * 64;
+  const __amdgpu_buffer_rsrc_t rq =
+      buffer_rsrc(q + static_cast<int64_t>(b0) * heads * d, static_cast<int64_t>(min(16, b - b0)) * heads * d * 2);
+  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(Wk + static_cast<int64_t>(jb0) * E,
+                                                static_cast<int64_t>(min(64, r - jb0)) * E * sizeof(WT));
+  const uint32_t qoff = static_cast<uint32_t>((((lane & 15) * heads + h) * d + kq) * 2);
+  const uint32_t woff = static_cast<uint32_t>(((j - jb0) * E + h * d + kq) * sizeof(WT));
   u32x4 av[DK], bv[DK];
 #pragma unroll
   for (int k = 0; k < DK; ++k) {
-    const int i = 32 * k + kq;
-    av[k] = u32x4{0u, 0u, 0u, 0u};
-    bv[k] = u32x4{0u, 0u, 0u, 0u};
-    if (bb < b) av[k] = *reinterpret_cast<const u32x4 *>(q + (static_cast<int64_t>(bb) * heads + h) * d + i);
-    if (j < r) {
-      if constexpr (sizeof(WT) == 2) {
-        bv[k] = *reinterpret_cast<const u32x4 *>(Wk + static_cast<int64_t>(j) * E + h * d + i);
-      } else {
-        const u32x2 c = *reinterpret_cast<const u32x2 *>(Wk + static_cast<int64_t>(j) * E + h * d + i);
-        bv[k] = u32x4{c.x, c.y, 0u, 0u};
-      }
+    av[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * k, 0, 0));
+    if constexpr (sizeof(WT) == 2) {
+      bv[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 64 * k, 0, 0));
+    } else {
+      const u32x2 c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, woff + 32 * k, 0, 0));
+      bv[k] = u32x4{c.x, c.y, 0u, 0u};
     }
   }
   // int8 W^u_k: the column scales of this lane's q elements, requested with
@@ -164,6 +178,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t *__rest
       sv[k][1] = *reinterpret_cast<const f32x4 *>(wscale + h * d + 32 * k + kq + 4);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);   // every operand load is issued before the products
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < DK; ++k) {
@@ -579,12 +594,6 @@ __device__ __forceinline__ u32x4 i4_order(u32x4 v) {
 }
 // Column (within its group of eight) held at K position p of the int4 order.
 __device__ __forceinline__ int i4_column(int p) { return (p >> 1) + 4 * (p & 1); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
-                                           static_cast<int>(n), 0x00020000);
-}
 
 // Template parameters: cache format CT, NHB 16-head blocks per workgroup, NKB
 // 32-column K blocks per wavefront (RW = 32 NKB columns), T tokens per tile
