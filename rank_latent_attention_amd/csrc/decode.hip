@@ -1468,18 +1468,18 @@ __global__ __launch_bounds__(256) void merge_f32_kernel(const float *__restrict_
   }
 }
 
-// O = sum over the JC chunk shares, 4 consecutive outputs per thread, the
-// loads of all chunks issued before the sum (n % 4 == 0).
-template <typename OT>
+// O = sum over the JC chunk shares, 4 consecutive outputs per thread
+// (n % 4 == 0).  The loads of the first MAXJC chunks are unconditional (a
+// chunk index past JC rereads the last chunk and is not summed), so all of
+// them are in flight before the first wait.
+template <typename OT, int MAXJC>
 __global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ opj,
                                                        OT *__restrict__ O, int64_t n, int JC) {
-  constexpr int MAXJC = 32;
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
   f32x4 v[MAXJC];
 #pragma unroll
-  for (int c = 0; c < MAXJC; ++c)
-    if (c < JC) v[c] = *reinterpret_cast<const f32x4 *>(opj + c * n + i);
+  for (int c = 0; c < MAXJC; ++c) v[c] = *reinterpret_cast<const f32x4 *>(opj + min(c, JC - 1) * n + i);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < MAXJC; ++c)
@@ -1923,10 +1923,17 @@ hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s
     const int64_t n = static_cast<int64_t>(a.b) * a.heads * a.d;
     const int JC = p.jc;
     const dim3 grid(static_cast<unsigned>((n / 4 + 255) / 256)), block(256);
-    if (a.o_dtype == QSVD_BF16)
-      finalize_kernel<uint16_t><<<grid, block, 0, s>>>(opj, static_cast<uint16_t *>(a.O), n, JC);
-    else
-      finalize_kernel<float><<<grid, block, 0, s>>>(opj, static_cast<float *>(a.O), n, JC);
+    auto run = [&](auto OTV, auto MJ) {
+      using OT = decltype(OTV);
+      finalize_kernel<OT, decltype(MJ)::value><<<grid, block, 0, s>>>(opj, static_cast<OT *>(a.O), n, JC);
+    };
+    auto pick = [&](auto OTV) {
+      if (JC <= 8) run(OTV, std::integral_constant<int, 8>{});
+      else if (JC <= 16) run(OTV, std::integral_constant<int, 16>{});
+      else run(OTV, std::integral_constant<int, 32>{});
+    };
+    if (a.o_dtype == QSVD_BF16) pick(uint16_t{});
+    else pick(float{});
     e = hipGetLastError();
   }
   return e;

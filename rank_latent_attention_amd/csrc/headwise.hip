@@ -396,6 +396,8 @@ __global__ __launch_bounds__(256) void headwise_merge_kernel(const float *__rest
                                                              const uint16_t *__restrict__ BV,
                                                              OT *__restrict__ O, int b, int heads, int S) {
   constexpr int PW = RV + 4;
+  constexpr int SB = 8;                            // splits whose loads are issued together
+  constexpr int CPL = (RV + kWave - 1) / kWave;    // O~ columns per lane
   __shared__ float om[4][RV];
   const int wl = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + wl;
@@ -403,47 +405,66 @@ __global__ __launch_bounds__(256) void headwise_merge_kernel(const float *__rest
   const int seq = w / heads, h = w % heads;
   const float *base = part + (static_cast<int64_t>(seq) * S * heads + h) * PW;
   const int64_t sstride = static_cast<int64_t>(heads) * PW;
-  float M = -INFINITY;
-  for (int s = lane; s < S; s += kWave) M = fmaxf(M, base[s * sstride]);
-  M = group_max<kWave>(M);
-  float den = 0.f;
-  for (int s = lane; s < S; s += kWave) {
-    const float ms = base[s * sstride];
-    den += ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M) * base[s * sstride + 1];
-  }
-  den = group_sum<kWave>(den);
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  constexpr int CPL = (RV + kWave - 1) / kWave;   // O~ columns per lane
-  float acc[CPL];
+  // One round of loads: (m, l) and the O~ row of the first SB splits (split
+  // indices past S reread the last split and are not used), and B_Vh as
+  // column pairs (lane: output columns 2 lane, 2 lane + 1 of every row).
+  float mv[SB], lv[SB], pr[SB][CPL];
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
-  for (int s = 0; s < S; ++s) {
+  for (int k = 0; k < SB; ++k) {
+    const float *src = base + min(k, S - 1) * sstride;
+    mv[k] = src[0];
+    lv[k] = src[1];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) pr[k][c] = src[4 + min(lane + kWave * c, RV - 1)];
+  }
+  const uint32_t *bv = reinterpret_cast<const uint32_t *>(BV + static_cast<int64_t>(h) * RV * kHd);
+  uint32_t wv[RV];
+#pragma unroll
+  for (int c = 0; c < RV; ++c) wv[c] = bv[c * (kHd / 2) + lane];
+  // log-sum-exp weights 2^(m_s - M) (every lane holds every split's (m, l))
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < SB; ++k)
+    if (k < S) M = fmaxf(M, mv[k]);
+  for (int s = SB; s < S; ++s) M = fmaxf(M, base[s * sstride]);
+  float den = 0.f, acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int k = 0; k < SB; ++k) {
+    if (k < S) {
+      const float wgt = mv[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[k] - M);
+      den = fmaf(wgt, lv[k], den);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wgt, pr[k][c], acc[c]);
+    }
+  }
+  for (int s = SB; s < S; ++s) {
     const float *src = base + s * sstride;
     const float ms = src[0];
     const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    den = fmaf(wgt, src[1], den);
 #pragma unroll
-    for (int k = 0; k < CPL; ++k)
-      if (lane + kWave * k < RV) acc[k] = fmaf(wgt, src[4 + lane + kWave * k], acc[k]);
+    for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wgt, src[4 + min(lane + kWave * c, RV - 1)], acc[c]);
   }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
-  for (int k = 0; k < CPL; ++k)
-    if (lane + kWave * k < RV) om[wl][lane + kWave * k] = acc[k] * inv;
+  for (int c = 0; c < CPL; ++c)
+    if (lane + kWave * c < RV) om[wl][lane + kWave * c] = acc[c] * inv;
   __builtin_amdgcn_wave_barrier();
-  const uint16_t *bv = BV + static_cast<int64_t>(h) * RV * kHd;
+  // o_h = O~_h B_Vh
   float a0 = 0.f, a1 = 0.f;
-#pragma unroll 16
+#pragma unroll
   for (int c = 0; c < RV; ++c) {
     const float oc = om[wl][c];
-    a0 = fmaf(oc, bf16_to_f32(bv[c * kHd + lane]), a0);
-    a1 = fmaf(oc, bf16_to_f32(bv[c * kHd + 64 + lane]), a1);
+    a0 = fmaf(oc, __uint_as_float(wv[c] << 16), a0);
+    a1 = fmaf(oc, __uint_as_float(wv[c] & 0xFFFF0000u), a1);
   }
-  OT *out = O + (static_cast<int64_t>(seq) * heads + h) * kHd;
+  OT *out = O + (static_cast<int64_t>(seq) * heads + h) * kHd + 2 * lane;
   if constexpr (sizeof(OT) == 2) {
-    out[lane] = f32_to_bf16(a0);
-    out[64 + lane] = f32_to_bf16(a1);
+    *reinterpret_cast<uint32_t *>(out) = pack_bf16x2(a0, a1);
   } else {
-    out[lane] = a0;
-    out[64 + lane] = a1;
+    *reinterpret_cast<float2 *>(out) = float2{a0, a1};
   }
 }
 
