@@ -296,6 +296,23 @@ def test_two_pass_decode(shape):
     assert np.array_equal(decode_case_on_gpu(cs, splits=5), got)
 
 
+@pytest.mark.parametrize("r,heads,b,L", [(160, 8, 3, 70), (224, 8, 17, 50)], ids=lambda v: str(v))
+def test_int8_up_projections_ragged(r, heads, b, L):
+    """int8 W^u over a bf16 cache whose latent width is not a multiple of the
+    absorb's 64-row block and whose batch is not a multiple of 16: the rows
+    past r and the sequences past b read as zero in the absorb and merge."""
+    d = 128
+    say(f"case: int8 W^u ragged, r={r} heads={heads} b={b} L={L}")
+    cs = synth.decode_case(heads * d, heads, d, r, b, L, dtype="bf16", hadamard=0, seed=97)
+    Wk_q, Wk_s = synth.int8_columns(values(cs.Wu_k, "bf16"))
+    Wv_q, Wv_s = synth.int8_columns(values(cs.Wu_v, "bf16"))
+    O = decode(dev(cs.q), q.BF16, dev(cs.C), q.BF16, dev(Wk_q), dev(Wv_q), q.I8, b, L, r, heads, d,
+               cs.softmax_scale, wsk=dev(Wk_s), wsv=dev(Wv_s))
+    ref = oracle.attend_explicit(values(cs.q, "bf16"), values(cs.C, "bf16"), oracle.dequant_cols(Wk_q, Wk_s),
+                                 oracle.dequant_cols(Wv_q, Wv_s), heads, d, cs.softmax_scale)
+    check_rows(host(O), ref, TOL_BF16, "int8 W^u ragged")
+
+
 def test_two_pass_with_int8_up_projections():
     """Two-pass decode of a bf16 cache with W^u stored as int8 columns (absorb and merge dequantise)."""
     heads, r, b, L, d = 40, 2304, 2, 700, 128
