@@ -352,7 +352,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
     float scale) {
   constexpr int NW = kFusedWaves, NT = 64 * NW;
   constexpr int RPW = (64 * MAXJ + NW - 1) / NW;   // latent rows per wavefront in step 1
-  constexpr int TB = 8;                            // token rows requested together
+  constexpr int TB = MAXJ == 1 ? 32 : 64 / MAXJ;   // token rows per wavefront held in registers
+  constexpr int KU = (64 * MAXJ + 7) / 8;          // W^u_v rows per thread in step 4 (NT / d >= 8)
   extern __shared__ float fs[];
   float *qs = fs;               // [r] q~
   float *wo = qs + r;           // [NW][r] per-wavefront O~
@@ -363,23 +364,46 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
   const int h = blockIdx.x, seq = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t E = static_cast<int64_t>(heads) * d;
+  const float *Cs = C + static_cast<int64_t>(seq) * L * r;
+
+  // Loads whose addresses do not depend on q~ go first: the W^u_k,h rows
+  // (step 1) and this wavefront's first TB token rows (step 2); this thread's
+  // W^u_v,h rows (step 4) are requested before the combine.  They go through buffer
+  // resources: rows past the end (tokens past L, latent rows past r) read as
+  // zero, the row offsets are wave-uniform scalar offsets, and no load sits
+  // behind a branch, so all of them are in flight together.  Columns past r
+  // or d read neighbouring values, which meet a zero query element (steps 1
+  // and 2) or are never stored.
+  const float *qh = q + (static_cast<int64_t>(seq) * heads + h) * d;
+  const float q0 = qh[min(lane, d - 1)], q1 = qh[min(lane + 64, d - 1)];
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(Wk + static_cast<int64_t>(h) * d, (r * E - h * d) * 4);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(Wv + static_cast<int64_t>(h) * d, (r * E - h * d) * 4);
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(Cs, L * r * 4);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform, for scalar offsets
+  float w0[RPW], w1[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int so = static_cast<int>((wave_s + NW * i) * E * 4);
+    w0[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, lane * 4, so, 0));
+    w1[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, lane * 4 + 256, so, 0));
+  }
+  float c[TB][MAXJ];
+  auto load_rows = [&](int64_t t0) {
+    const int vo = static_cast<int>(t0 * r * 4) + lane * 4;
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int k = 0; k < MAXJ; ++k)
+        c[u][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo + 256 * k, NW * u * r * 4, 0));
+  };
+  load_rows(wave);
 
   // ---- 1. absorbed query
   {
-    const float *qh = q + (static_cast<int64_t>(seq) * heads + h) * d;
-    const float q0 = lane < d ? qh[lane] : 0.f;
-    const float q1 = lane + 64 < d ? qh[lane + 64] : 0.f;
-    float w0[RPW], w1[RPW];
+    const float qa = lane < d ? q0 : 0.f, qb = lane + 64 < d ? q1 : 0.f;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      const int k = min(wave + NW * i, r - 1);
-      const float *row = Wk + static_cast<int64_t>(k) * E + static_cast<int64_t>(h) * d;
-      w0[i] = lane < d ? row[lane] : 0.f;
-      w1[i] = lane + 64 < d ? row[lane + 64] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      float v = fmaf(w1[i], q1, w0[i] * q0);
+      float v = fmaf(w1[i], qb, w0[i] * qa);
       v = dpp_reduce<32, false>(v);
       v += __shfl_xor(v, 32, 64);
       const int k = wave + NW * i;
@@ -388,43 +412,46 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
   }
   __syncthreads();
 
-  // ---- 2. this wavefront's tokens
+  // ---- 2. this wavefront's tokens t = wave + NW i, TB at a time: the batch's
+  // scores, its maximum, one rescale of (O~, l), then the batch's p C
   float qv[MAXJ], o[MAXJ];
 #pragma unroll
   for (int k = 0; k < MAXJ; ++k) {
     const int j = lane + 64 * k;
-    qv[k] = j < r ? qs[j] : 0.f;
+    qv[k] = j < r ? qs[j] : 0.f;   // columns past r add nothing to the scores
     o[k] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  for (int64_t tb = wave; tb < L; tb += NW * TB) {
-    float c[TB][MAXJ];
+  for (int64_t t0 = wave; t0 < L; t0 += NW * TB) {
+    if (t0 != wave) load_rows(t0);
+    const int nb = static_cast<int>(std::min<int64_t>(TB, (L - t0 + NW - 1) / NW));   // rows inside L
+    float sc[TB];
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
-      const int64_t t = min(tb + NW * u, L - 1);
-      const float *row = C + (static_cast<int64_t>(seq) * L + t) * r;
+      float v = 0.f;
 #pragma unroll
-      for (int k = 0; k < MAXJ; ++k) {
-        const int j = lane + 64 * k;
-        c[u][k] = j < r ? row[j] : 0.f;
+      for (int k = 0; k < MAXJ; ++k) v = fmaf(c[u][k], qv[k], v);
+      v = dpp_reduce<32, false>(v);
+      sc[u] = v + __shfl_xor(v, 32, 64);
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+      if (u < nb) mn = fmaxf(mn, sc[u]);
+    const float alpha = exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int k = 0; k < MAXJ; ++k) o[k] *= alpha;
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      if (u < nb) {
+        const float pe = exp2f(sc[u] - mn);
+        l += pe;
+#pragma unroll
+        for (int k = 0; k < MAXJ; ++k) o[k] = fmaf(pe, c[u][k], o[k]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      if (tb + NW * u >= L) break;
-      float sc = 0.f;
-#pragma unroll
-      for (int k = 0; k < MAXJ; ++k) sc = fmaf(c[u][k], qv[k], sc);
-      sc = dpp_reduce<32, false>(sc);
-      sc += __shfl_xor(sc, 32, 64);
-      const float mn = fmaxf(m, sc);
-      const float alpha = exp2f(m - mn);
-      const float pe = exp2f(sc - mn);
-      l = fmaf(l, alpha, pe);
-#pragma unroll
-      for (int k = 0; k < MAXJ; ++k) o[k] = fmaf(o[k], alpha, pe * c[u][k]);
-      m = mn;
-    }
+    m = mn;
   }
 #pragma unroll
   for (int k = 0; k < MAXJ; ++k) {
@@ -435,6 +462,13 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
     wm[wave] = m;
     wl[wave] = l;
   }
+  // this thread's W^u_v,h rows g, g + G, ... (rows past r read as zero)
+  const int G = NT / d, cc = tid % d, g = tid / d;
+  float wv[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u)
+    wv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, static_cast<int>((g * E + cc) * 4),
+                                                                 static_cast<int>(G * u * E * 4), 0));
   __syncthreads();
 
   // ---- 3. combine the wavefronts (L >= 1: the maximum is finite)
@@ -458,21 +492,12 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
   }
   __syncthreads();
 
-  // ---- 4. output projection
-  const int G = NT / d;
-  const int cc = tid % d, g = tid / d;
+  // ---- 4. output projection: thread (column cc, rows g, g + G, ...), the G
+  // row groups summed through LDS in a fixed order
   float acc = 0.f;
-  for (int k0 = g; k0 < r; k0 += 4 * G) {
-    float wv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = min(k0 + G * u, r - 1);
-      wv[u] = Wv[static_cast<int64_t>(k) * E + static_cast<int64_t>(h) * d + cc];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (k0 + G * u < r) acc = fmaf(ot[k0 + G * u], wv[u], acc);
-  }
+  for (int u = 0; u < KU; ++u)
+    if (g + G * u < r) acc = fmaf(ot[g + G * u], wv[u], acc);
   red[tid] = acc;
   __syncthreads();
   if (tid < d) {
