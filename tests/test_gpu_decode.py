@@ -72,6 +72,7 @@ def test_fp32_split_invariance(L, splits):
     (128, 2, 64, 40, 2, 5),        # fewer tokens than wavefronts
     (1024, 16, 64, 200, 2, 1),     # a single cached latent
     (768, 6, 128, 130, 2, 333),    # r not a multiple of 64
+    (512, 4, 128, 64, 2, 1000),    # one column block: two 32-token batches per wavefront, the last ragged
 ], ids=lambda s: "E{}h{}d{}r{}b{}L{}".format(*s))
 def test_fp32_one_launch_matches_split_path(shape):
     """Small float32 problems run as one launch per step when the library
