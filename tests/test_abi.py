@@ -119,6 +119,10 @@ def test_decode_validation():
     assert st_dec(wdt=q.F32) == -2
     assert st_dec(wdt=q.I8) == -1                 # int8 W^u needs column scales
     assert st_dec(wsk=FAKE, wsv=FAKE) == -1       # bf16 W^u takes none
+    odd = ctypes.c_void_p((1 << 20) + 4)          # 4-byte but not 16-byte aligned
+    assert st_dec(wdt=q.I8, wsk=odd, wsv=FAKE) == -1   # W^u scales are read 16 bytes at a time
+    assert st_dec(wdt=q.I8, wsk=FAKE, wsv=odd) == -1
+    assert "misaligned" in q.qsvd_last_error()
     assert st_dec(cdt=q.F32, qdt=q.F32, wdt=q.F32, odt=q.BF16) == -2
     assert st_dec(scale=0.0) == -1
     assert st_dec(scale=float("nan")) == -1
