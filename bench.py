@@ -601,8 +601,8 @@ def tiny_leg(q, torch, synth, dev, args):
     cache_bytes = cs.b * cs.L * cs.r * 4
     gbs = cache_bytes / (ms * 1e-3) / 1e9
     return {"workload": f"decode step, {synth.CONFIGS[0].name}", "us_per_step": round(ms * 1e3, 2),
-            "roofline": {"bound": "hbm", "kernel": "whole step (launch-latency bound: four launches "
-                                                   "over a 197 KB cache)",
+            "roofline": {"bound": "hbm", "kernel": "whole step (latency bound: one launch, "
+                                                   "decode_f32_fused_kernel, over a 197 KB cache)",
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 6), "algorithmic_bytes": cache_bytes},
             "kernels_note": "launch-boundary times of a host-bound loop: the gap until the next "
