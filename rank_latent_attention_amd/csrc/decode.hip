@@ -352,7 +352,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
     float scale) {
   constexpr int NW = kFusedWaves, NT = 64 * NW;
   constexpr int RPW = (64 * MAXJ + NW - 1) / NW;   // latent rows per wavefront in step 1
-  constexpr int TB = MAXJ == 1 ? 32 : 64 / MAXJ;   // token rows per wavefront held in registers
+  constexpr int CPL = 4 * MAXJ;                    // latent columns per lane (16 lanes per token)
+  constexpr int TPG = 64 / CPL;                    // tokens per 16-lane group and batch
+  constexpr int TBW = 4 * TPG;                     // tokens per wavefront and batch
   constexpr int KU = (64 * MAXJ + 7) / 8;          // W^u_v rows per thread in step 4 (NT / d >= 8)
   extern __shared__ float fs[];
   float *qs = fs;               // [r] q~
@@ -387,16 +389,23 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
     w0[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, lane * 4, so, 0));
     w1[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, lane * 4 + 256, so, 0));
   }
-  float c[TB][MAXJ];
-  auto load_rows = [&](int64_t t0) {
-    const int vo = static_cast<int>(t0 * r * 4) + lane * 4;
+  // Step 2's layout: the wavefront takes four tokens at a time, one per
+  // 16-lane group; lane li of group grp holds columns li, li + 16, ... of its
+  // token (16 consecutive values per group and load).  Batch i0 of this
+  // wavefront: group grp takes tokens wave + NW (i0 + 4 u + grp), u < TPG.
+  const int grp = lane >> 4, li = lane & 15;
+  float c[TPG][CPL];
+  auto load_rows = [&](int64_t i0) {
 #pragma unroll
-    for (int u = 0; u < TB; ++u)
+    for (int u = 0; u < TPG; ++u) {
+      const int64_t tok = wave + NW * (i0 + 4 * u + grp);
+      const int vo = static_cast<int>(std::min<int64_t>(tok, L) * r + li) * 4;   // rows at L read zero
 #pragma unroll
-      for (int k = 0; k < MAXJ; ++k)
-        c[u][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo + 256 * k, NW * u * r * 4, 0));
+      for (int k = 0; k < CPL; ++k)
+        c[u][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo + 64 * k, 0, 0));
+    }
   };
-  load_rows(wave);
+  load_rows(0);
 
   // ---- 1. absorbed query
   {
@@ -412,51 +421,61 @@ __global__ __launch_bounds__(64 * kFusedWaves) void decode_f32_fused_kernel(
   }
   __syncthreads();
 
-  // ---- 2. this wavefront's tokens t = wave + NW i, TB at a time: the batch's
-  // scores, its maximum, one rescale of (O~, l), then the batch's p C
-  float qv[MAXJ], o[MAXJ];
+  // ---- 2. this wavefront's tokens, TBW per batch: 16-lane dot products (four
+  // tokens per DPP reduction), the batch maximum over all four groups, one
+  // rescale of (O~, l), then p C per group; the groups' partial O~ and l are
+  // added at the end (they share the running maximum)
+  float qv[CPL], o[CPL];
 #pragma unroll
-  for (int k = 0; k < MAXJ; ++k) {
-    const int j = lane + 64 * k;
+  for (int k = 0; k < CPL; ++k) {
+    const int j = li + 16 * k;
     qv[k] = j < r ? qs[j] : 0.f;   // columns past r add nothing to the scores
     o[k] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  for (int64_t t0 = wave; t0 < L; t0 += NW * TB) {
-    if (t0 != wave) load_rows(t0);
-    const int nb = static_cast<int>(std::min<int64_t>(TB, (L - t0 + NW - 1) / NW));   // rows inside L
-    float sc[TB];
+  for (int64_t i0 = 0; wave + NW * i0 < L; i0 += TBW) {
+    if (i0 != 0) load_rows(i0);
+    float sc[TPG];
 #pragma unroll
-    for (int u = 0; u < TB; ++u) {
+    for (int u = 0; u < TPG; ++u) {
       float v = 0.f;
 #pragma unroll
-      for (int k = 0; k < MAXJ; ++k) v = fmaf(c[u][k], qv[k], v);
-      v = dpp_reduce<32, false>(v);
-      sc[u] = v + __shfl_xor(v, 32, 64);
+      for (int k = 0; k < CPL; ++k) v = fmaf(c[u][k], qv[k], v);
+      v = dpp_reduce<16, false>(v);
+      sc[u] = wave + NW * (i0 + 4 * u + grp) < L ? v : -INFINITY;
     }
     float mn = m;
 #pragma unroll
-    for (int u = 0; u < TB; ++u)
-      if (u < nb) mn = fmaxf(mn, sc[u]);
+    for (int u = 0; u < TPG; ++u) mn = fmaxf(mn, sc[u]);
+    mn = fmaxf(mn, __shfl_xor(mn, 16, 64));
+    mn = fmaxf(mn, __shfl_xor(mn, 32, 64));   // finite: the batch's first token is inside L
     const float alpha = exp2f(m - mn);
     l *= alpha;
 #pragma unroll
-    for (int k = 0; k < MAXJ; ++k) o[k] *= alpha;
+    for (int k = 0; k < CPL; ++k) o[k] *= alpha;
 #pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      if (u < nb) {
-        const float pe = exp2f(sc[u] - mn);
-        l += pe;
+    for (int u = 0; u < TPG; ++u) {
+      const float pe = exp2f(sc[u] - mn);   // 0 for tokens past L
+      l += pe;
 #pragma unroll
-        for (int k = 0; k < MAXJ; ++k) o[k] = fmaf(pe, c[u][k], o[k]);
-      }
+      for (int k = 0; k < CPL; ++k) o[k] = fmaf(pe, c[u][k], o[k]);
     }
     m = mn;
   }
+  // the four groups' shares (fixed order: xor 16, then xor 32)
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
 #pragma unroll
-  for (int k = 0; k < MAXJ; ++k) {
-    const int j = lane + 64 * k;
-    if (j < r) wo[wave * r + j] = o[k];
+  for (int k = 0; k < CPL; ++k) {
+    o[k] += __shfl_xor(o[k], 16, 64);
+    o[k] += __shfl_xor(o[k], 32, 64);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int j = li + 16 * k;
+      if (j < r) wo[wave * r + j] = o[k];
+    }
   }
   if (lane == 0) {
     wm[wave] = m;
