@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void stream_f32_kernel(const float *__restrict
 //   1. q~ = scale log2e W^u_k,h q_h: wavefront w computes latent rows w,
 //      w + 16, ... (one 64-lane dot product each, every row requested first),
 //   2. wavefront w streams tokens w, w + 16, ... with its own online softmax,
-//      TB rows requested together,
+//      four tokens at a time (one per 16-lane group), TBW per batch,
 //   3. the 16 states are combined in LDS by log-sum-exp weights (fixed order),
 //   4. O = (O~ / l) W^u_v,h: thread (column c, row group g) sums the rows
 //      g, g + G, ..., and the G row groups are summed in LDS.
