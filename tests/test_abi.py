@@ -252,3 +252,31 @@ def test_latent_width_rule_matches_the_header():
         for dt, g in ((q.BF16, 32), (q.I8, 64), (q.I4, 128)):
             ok = q.qsvd_decode_workspace_bytes(2, 100, r, 8, 128, dt, 0) > 0
             assert ok == accepted(r, g), (r, dt)
+
+
+def test_last_error_is_per_thread():
+    """qsvd_last_error() is thread-local: threads that fail validation at the
+    same time each read back their own message (ctypes drops the GIL around
+    the calls, so they run concurrently in the library)."""
+    import threading
+    n, reps = 8, 200
+    start = threading.Barrier(n)
+    bad = []
+
+    def worker(i):
+        start.wait()
+        for _ in range(reps):
+            if st_dec(heads=300 + i) != -1:
+                bad.append((i, "status"))
+                return
+            msg = q.qsvd_last_error()
+            if f"heads = {300 + i}" not in msg:
+                bad.append((i, msg))
+                return
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(n)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad, bad[:3]
