@@ -135,3 +135,66 @@ def test_concurrent_streams_match_sequential():
         torch.cuda.synchronize()
         assert torch.equal(O1, ref1) and torch.equal(O2, ref2), rnd
     say("  4 rounds of interleaved launches equal the sequential results")
+
+
+def test_concurrent_host_threads_match_sequential():
+    """Four host threads, each with its own stream, output and workspace, issue decode steps of
+    different kinds at the same time (bf16 single pass, bf16 two passes, per-head latents, float32
+    one launch).  ctypes drops the GIL around the calls, so the library's host side (validation,
+    planning, the per-thread launch-attribute records) runs concurrently; every result equals the
+    same call made alone."""
+    import threading
+    import torch
+    say("case: concurrent decode calls from four host threads")
+    c1 = synth.decode_case(1024, 8, 128, 512, 3, 900, dtype="bf16", hadamard=128, seed=81)
+    c2 = synth.decode_case(5120, 40, 128, 2304, 1, 300, dtype="bf16", hadamard=128, seed=82)
+    hc = synth.headwise_case(2, 700, 8, 128, 64, 64, seed=83)
+    c4 = synth.decode_case(256, 4, 64, 96, 1, 512, dtype="f32", seed=84)
+    calls = []
+
+    def add_decode(cs, dt, b, L, r, heads, d):
+        C, Wk, Wv, qv = dev(cs.C), dev(cs.Wu_k), dev(cs.Wu_v), dev(cs.q)
+        O = empty((b, heads, d), torch.float32)
+        ws = workspace(q.qsvd_decode_workspace_bytes(b, L, r, heads, d, dt, 0))
+        calls.append((O, lambda s: q.qsvd_decode_attn(qv, dt, C, dt, None, 0, Wk, Wv, dt, None, None, b, L, r,
+                                                      heads, d, cs.softmax_scale, 0, O, q.F32, ws,
+                                                      stream=s)))
+
+    add_decode(c1, q.BF16, 3, 900, 512, 8, 128)
+    add_decode(c2, q.BF16, 1, 300, 2304, 40, 128)
+    Ch, BK, BV, qh = dev(hc.C), dev(hc.BK_t), dev(hc.BV), dev(hc.q)
+    Oh = empty((2, 8, 128), torch.float32)
+    wsh = workspace(q.qsvd_decode_headwise_workspace_bytes(2, 700, 8, 128, 64, 64, 0))
+    calls.append((Oh, lambda s: q.qsvd_decode_attn_headwise(qh, q.BF16, Ch, q.BF16, BK, BV, q.BF16, 2, 700, 8,
+                                                            128, 64, 64, hc.softmax_scale, None, None, 0, Oh,
+                                                            q.F32, wsh, stream=s)))
+    add_decode(c4, q.F32, 1, 512, 96, 4, 64)
+    refs = []
+    for O, call in calls:
+        call(None)
+        torch.cuda.synchronize()
+        refs.append(O.clone())
+        O.zero_()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in calls]
+    start = threading.Barrier(len(calls))
+    errors = []
+
+    def worker(i):
+        try:
+            start.wait()
+            for _ in range(20):
+                calls[i][1](streams[i].cuda_stream)
+        except Exception as e:   # reported below, on the main thread
+            errors.append((i, repr(e)))
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(len(calls))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, (O, _) in enumerate(calls):
+        assert torch.equal(O, refs[i]), i
+    say("  20 calls per thread on four streams equal the sequential results")
