@@ -89,6 +89,28 @@ def test_fp32_one_launch_matches_split_path(shape):
     assert oracle.rel_l2(one, split) <= TOL_F32
 
 
+@pytest.mark.parametrize("shape,fused", [
+    # E, heads, d, r, b, L: the limits of the one-launch rule, then one past each limit
+    ((1024, 16, 64, 256, 16, 1024), True),    # b heads = 256, r = 256, L = 1024
+    ((1024, 16, 64, 256, 17, 64), False),     # b heads = 272
+    ((512, 8, 64, 288, 2, 100), False),       # r = 288
+    ((512, 8, 64, 96, 2, 1025), False),       # L = 1025
+], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else ("fused" if v else "split"))
+def test_fp32_one_launch_limits(shape, fused):
+    """The one-launch float32 path runs exactly inside its limits (library-chosen
+    splits, r <= 256, L <= 1024, b heads <= 256) and the split path just past
+    each of them; both match the oracle."""
+    E, heads, d, r, b, L = shape
+    say(f"case: fp32 one-launch limits {shape} fused={fused}")
+    cs = synth.decode_case(E, heads, d, r, b, L, dtype="f32", seed=E + r + L + b)
+    with q.timing(max_launches=16) as tm:
+        got = decode_case_on_gpu(cs)
+    names = set(tm.result)
+    assert names == ({"decode_fused"} if fused else {"decode_absorb", "decode_stream", "decode_merge",
+                                                      "decode_finalize"}), names
+    check_rows(got, oracle_out(cs), TOL_F32, "fp32 limits")
+
+
 # ------------------------------------------------------------------ bf16 path
 BF16_SHAPES = [
     # E, heads, d, r, b, L
