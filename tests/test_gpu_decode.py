@@ -336,6 +336,28 @@ def test_int8_up_projections_ragged(r, heads, b, L):
     check_rows(host(O), ref, TOL_BF16, "int8 W^u ragged")
 
 
+@pytest.mark.parametrize("heads,r,wide", [
+    (40, 2304, True),     # the 13B shape
+    (64, 1792, True),     # the narrowest latent and the most heads of the two-pass rule
+    (32, 2304, False),    # two head groups: one pass
+    (40, 1536, False),    # six K blocks per wavefront: one pass with 32-head groups
+    (72, 2048, False),    # more heads than the two-pass kernels hold: one pass, five head groups
+], ids=lambda v: str(v))
+def test_two_pass_rule(heads, r, wide):
+    """bf16 caches whose single pass would split 33..64 heads into three or
+    more groups at 7..9 K blocks per wavefront take the two passes; the
+    neighbouring shapes take the single pass.  Both match the oracle."""
+    d, b, L = 128, 1, 200
+    say(f"case: two-pass rule heads={heads} r={r} wide={wide}")
+    cs = synth.decode_case(heads * d, heads, d, r, b, L, dtype="bf16", hadamard=128, seed=heads + r)
+    with q.timing(max_launches=16) as tm:
+        got = decode_case_on_gpu(cs)
+    names = set(tm.result)
+    assert ("decode_scores" in names and "decode_values" in names) == wide, names
+    assert ("decode_stream" in names) == (not wide), names
+    check_rows(got, oracle_out(cs), TOL_BF16, "two-pass rule")
+
+
 def test_two_pass_with_int8_up_projections():
     """Two-pass decode of a bf16 cache with W^u stored as int8 columns (absorb and merge dequantise)."""
     heads, r, b, L, d = 40, 2304, 2, 700, 128
