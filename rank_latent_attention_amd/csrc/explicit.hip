@@ -28,6 +28,8 @@
 #include "dma_pipe.h"
 #include "qsvd_internal.h"
 
+#include <algorithm>
+
 #include <cmath>
 #include <cstdint>
 
@@ -326,16 +328,42 @@ __global__ __launch_bounds__(256) void explicit_merge_kernel(const float *__rest
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (w >= b * heads) return;   // uniform per wavefront; no barrier follows
   const int seq = w / heads, h = w % heads;
+  // Tiles are read TB at a time with unconditional loads (an index past the
+  // last tile rereads it and is not used), so each batch is one memory round
+  // trip; the sums still run over the tiles in order.
+  constexpr int TB = 8;
+  auto src_of = [&](int64_t i) {
+    return part + ((seq * ntiles + std::min<int64_t>(i, ntiles - 1)) * heads + h) * kPartFloats;
+  };
   float M = -INFINITY;
-  for (int64_t i = 0; i < ntiles; ++i)
-    M = fmaxf(M, part[((seq * ntiles + i) * heads + h) * kPartFloats]);
+  for (int64_t i0 = 0; i0 < ntiles; i0 += TB) {
+    float mv[TB];
+#pragma unroll
+    for (int k = 0; k < TB; ++k) mv[k] = src_of(i0 + k)[0];
+#pragma unroll
+    for (int k = 0; k < TB; ++k)
+      if (i0 + k < ntiles) M = fmaxf(M, mv[k]);
+  }
   float den = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int64_t i = 0; i < ntiles; ++i) {
-    const float *src = part + ((seq * ntiles + i) * heads + h) * kPartFloats;
-    const float wgt = __builtin_amdgcn_exp2f(src[0] - M);
-    den = fmaf(wgt, src[1], den);
-    o0 = fmaf(wgt, src[4 + lane], o0);
-    o1 = fmaf(wgt, src[4 + 64 + lane], o1);
+  for (int64_t i0 = 0; i0 < ntiles; i0 += TB) {
+    float mv[TB], lv[TB], a0[TB], a1[TB];
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+      const float *src = src_of(i0 + k);
+      mv[k] = src[0];
+      lv[k] = src[1];
+      a0[k] = src[4 + lane];
+      a1[k] = src[4 + 64 + lane];
+    }
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+      if (i0 + k < ntiles) {
+        const float wgt = __builtin_amdgcn_exp2f(mv[k] - M);
+        den = fmaf(wgt, lv[k], den);
+        o0 = fmaf(wgt, a0[k], o0);
+        o1 = fmaf(wgt, a1[k], o1);
+      }
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   OT *out = O + (static_cast<int64_t>(seq) * heads + h) * kD;
